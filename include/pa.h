@@ -1,0 +1,277 @@
+/*
+ * pa.h -- C ABI of a paged KV-cache decode library for AMD Instinct MI355X
+ * (CDNA4, gfx950).
+ *
+ * Three pages describe the method; they are cited by title:
+ *   [PA-mem]    "Deep dive into the nano-vLLM inference engine architecture:
+ *               PagedAttention memory management" (blog.hotdry.top, 2026-02-02)
+ *   [nano-KV]   "Deep analysis of nano-vLLM's paged KV cache and memory
+ *               optimisation architecture" (blog.hotdry.top, 2026-02-02)
+ *   [vLLM-core] "vLLM core architecture: PagedAttention principle, KV Cache
+ *               management, continuous batching"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every call returns pa_status; PA_OK is 0.  On failure, pa_last_error()
+ *    returns a message for the calling thread.  No C++ exception crosses the
+ *    ABI.
+ *  - Device calls take plain device pointers and a HIP stream (hipStream_t
+ *    passed as void*; NULL means the default stream).  They only enqueue work
+ *    and return; they never allocate device memory and never synchronise,
+ *    except in validation mode (pa_set_validate), which copies the metadata
+ *    to the host and checks it before launching.  All argument checks happen
+ *    before any launch: a call that fails launches nothing.  Faults inside a
+ *    kernel surface as a HIP error at the caller's next synchronisation.
+ *  - The caller owns every device buffer, including the decode workspace.
+ *  - Element type of q, k, v, caches and out is IEEE binary16 (fp16).  Device
+ *    pointers to fp16 data must be 16-byte aligned.
+ *
+ * Cache layout (reading of [nano-KV] "Core mechanism of the paged KV cache",
+ * which flattens the cache into token slots, and of [PA-mem] "PagedAttention:
+ * the operating system's memory wisdom", which cuts it into fixed-size
+ * blocks): one tensor for keys and one for values, each
+ *     fp16 [num_blocks][block_size][num_kv_heads][head_dim], contiguous.
+ * Slot s is row (s % block_size) of physical block (s / block_size).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,           /* a required pointer is NULL                 */
+    PA_ERR_SHAPE = 2,          /* inconsistent or non-positive sizes          */
+    PA_ERR_ALIGN = 3,          /* a device pointer is not 16-byte aligned     */
+    PA_ERR_UNSUPPORTED = 4,    /* head_dim / block_size / group not built     */
+    PA_ERR_RANGE = 5,          /* a value outside its allowed range           */
+    PA_ERR_WORKSPACE = 6,      /* decode workspace missing or too small       */
+    PA_ERR_OUT_OF_BLOCKS = 7,  /* allocator: no free block left               */
+    PA_ERR_SEQ_LIMIT = 8,      /* allocator: max_blocks_per_seq reached       */
+    PA_ERR_UNKNOWN_SEQ = 9,    /* allocator: no such sequence                 */
+    PA_ERR_SEQ_EXISTS = 10,    /* allocator: sequence id already in use       */
+    PA_ERR_HIP = 11            /* a HIP runtime call failed                   */
+} pa_status;
+
+typedef struct pa_cache_desc {
+    int32_t num_blocks;        /* physical blocks in the pool                 */
+    int32_t block_size;        /* token slots per block: 8, 16, 32 or 64      */
+    int32_t num_kv_heads;      /* KV heads per token                          */
+    int32_t head_dim;          /* 64 or 128                                   */
+} pa_cache_desc;
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+/* Turn validation mode on (nonzero) or off.  Its initial value comes from the
+ * environment variable PA_VALIDATE ("1" = on).  In validation mode the device
+ * calls copy their integer metadata to the host, synchronise the stream, and
+ * reject out-of-range or duplicate entries with PA_ERR_RANGE before any
+ * launch.  Returns the previous setting. */
+int pa_set_validate(int on);
+
+/* ----------------------------------------------------------------------- */
+/* Store: write each new token's K and V rows into its cache slot.
+ *
+ * Source: [nano-KV] "Core mechanism of the paged KV cache" -- every new key
+ * and value row goes to the cache slot that a per-token slot mapping names.
+ *
+ *   k, v          device fp16 [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping  device int32 [num_tokens]; slot < 0 means "skip this token"
+ *                 (padding).  Non-negative slots must be distinct and below
+ *                 num_blocks * block_size; a slot at or beyond that bound is
+ *                 skipped by the kernel (and rejected in validation mode).
+ *   k_cache, v_cache  device fp16 caches described by *cache (written)
+ *
+ * The copy moves raw 16-bit patterns: every bit, NaN payloads included, lands
+ * unchanged.  num_tokens == 0 is valid and launches nothing.  Works for any
+ * head_dim that is a multiple of 8.
+ */
+pa_status pa_store_kvcache(const void* k, const void* v,
+                           const int32_t* slot_mapping, int32_t num_tokens,
+                           void* k_cache, void* v_cache,
+                           const pa_cache_desc* cache, void* hip_stream);
+
+/* ----------------------------------------------------------------------- */
+/* Copy whole physical blocks (copy-on-write of a shared block).
+ *
+ * Source: [vLLM-core] section 2 ("KV Cache management"), copy-on-write item:
+ * a page shared by several requests is duplicated only when one of them is
+ * about to modify it.
+ *
+ *   src_dst   device int32 [num_pairs][2]: copy block src_dst[i][0] into block
+ *             src_dst[i][1], every slot, every head, in both caches.
+ *
+ * Pairs run concurrently: no destination may appear twice or also appear as a
+ * source (the allocator's copy-on-write pairs always satisfy this).  Pairs
+ * with an out-of-range block are skipped by the kernel (and rejected in
+ * validation mode).  num_pairs == 0 is valid and launches nothing.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cache,
+                         const int32_t* src_dst, int32_t num_pairs, void* hip_stream);
+
+/* ----------------------------------------------------------------------- */
+/* Decode: single-query attention of every sequence over its paged context.
+ *
+ * Sources: [vLLM-core] section 1 ("PagedAttention: inspiration from virtual
+ * memory") -- a logically contiguous cache stored in scattered physical pages
+ * reached through a per-sequence page table; [PA-mem] "PagedAttention: the
+ * operating system's memory wisdom" -- the per-sequence block table maps
+ * logical positions to physical blocks; [nano-KV] "Engineering: configuration
+ * and monitoring" -- decode attention reads the paged cache (standard
+ * attention being the plain fallback).
+ *
+ * For every sequence s and query head h (KV head g = h / (num_q_heads /
+ * num_kv_heads)), with L = context_lens[s]:
+ *     z_p   = scale * dot(q[s][h], K[s, p, g])          p = 0 .. L-1
+ *     out[s][h] = sum_p softmax(z)_p * V[s, p, g]
+ * where K[s, p, g] is row (p % block_size), head g of physical block
+ * block_tables[s][p / block_size].  Accumulation is fp32; the output is
+ * rounded to fp16 (round to nearest even) once.  L == 0 gives a zero row.
+ *
+ *   q              device fp16 [num_seqs][num_q_heads][head_dim]
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]; only the first
+ *                  ceil(L / block_size) entries of a row are read.  Entries
+ *                  outside [0, num_blocks) are treated as holding no tokens
+ *                  (and rejected in validation mode).
+ *   context_lens   device int32 [num_seqs]; each must be at most
+ *                  max_context_len and at most max_blocks_per_seq*block_size
+ *                  (larger values are clamped; rejected in validation mode).
+ *   max_context_len  host upper bound of context_lens; sizes the launch.
+ *   scale          softmax scale (commonly 1/sqrt(head_dim)).
+ *   out            device fp16 [num_seqs][num_q_heads][head_dim] (written)
+ *   partition_tokens  tokens per split-K partition; 0 picks one from the
+ *                  shapes.  Must be 0 or a multiple of 16 in [16, 4096].
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
+ *                  bytes with the same shape arguments, 256-byte aligned; may
+ *                  be NULL when that size is 0.  Its contents on entry do not
+ *                  matter.
+ *
+ * Supported: head_dim 64 or 128; block_size 8, 16, 32 or 64; num_q_heads a
+ * multiple of num_kv_heads with a group size of 1, 2, 4 or 8.  Other shapes
+ * return PA_ERR_UNSUPPORTED.  Results depend only on logical token order, not
+ * on which physical blocks hold the tokens: moving blocks (and rewriting the
+ * tables to match) gives bitwise identical output.
+ */
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const pa_cache_desc* cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t max_context_len, float scale,
+                    void* out, int32_t partition_tokens,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of workspace pa_decode needs for these shapes (0 when every sequence
+ * fits one partition).  Returns 0 for unsupported or invalid shapes too. */
+size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_tokens);
+
+/* The partition size pa_decode uses for these shapes (resolves 0 = auto).
+ * Returns 0 for invalid shapes. */
+int32_t pa_decode_partition_tokens(const pa_cache_desc* cache, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_context_len,
+                                   int32_t partition_tokens);
+
+/* ----------------------------------------------------------------------- */
+/* Host-side block allocator (the block manager).
+ *
+ * Sources: [PA-mem] "PagedAttention: the operating system's memory wisdom"
+ * (a free-block list plus a per-sequence logical-to-physical table; initial
+ * blocks on arrival, a new block whenever the current one fills); [PA-mem]
+ * "Continuous batching and memory management working together" (a finished
+ * request returns all its blocks at once); [vLLM-core] section 2 ("KV Cache
+ * management": prefix pages shared between requests, copy-on-write, and
+ * reference counts so that a shared page is not released while in use).
+ *
+ * Policy: the free list is FIFO (blocks taken from the front, returned to
+ * the back in logical order); initial_free_order, if not NULL, is a
+ * permutation of [0, num_blocks) giving its first order, else 0..n-1.
+ * Every operation either succeeds completely or fails with the state
+ * unchanged.  Host memory only; one allocator must not be used by two threads
+ * at once.  Sequence ids are arbitrary int64 values.
+ */
+typedef struct pa_allocator pa_allocator;
+
+typedef struct pa_alloc_stats {
+    int32_t num_blocks;
+    int32_t free_blocks;
+    int32_t used_blocks;            /* reference count > 0                    */
+    int32_t shared_blocks;          /* reference count > 1                    */
+    int64_t cow_copies;             /* copy-on-write pairs handed out so far  */
+    int64_t live_seqs;
+    int64_t logical_tokens;         /* sum of sequence lengths                */
+    int64_t stored_tokens;          /* filled slots of used blocks            */
+    double utilisation;             /* used_blocks / num_blocks               */
+    double internal_fragmentation;  /* empty slots / slots of used blocks     */
+} pa_alloc_stats;
+
+/* Create an allocator.  block_size and max_blocks_per_seq must be positive. */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                          int32_t max_blocks_per_seq,
+                          const int32_t* initial_free_order, pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+
+/* Register sequence `seq` holding n_tokens tokens (n_tokens >= 0); takes
+ * ceil(n_tokens / block_size) blocks.  slots_out (nullable, host int32
+ * [n_tokens]) receives the slot of every token in order. */
+pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq, int32_t n_tokens,
+                           int32_t* slots_out);
+
+/* `child` starts as a copy of `parent`, sharing (and counting) every block. */
+pa_status pa_alloc_fork(pa_allocator* a, int64_t parent, int64_t child);
+
+/* Reserve the slot of the sequence's next token.  A fresh block is taken when
+ * the last block is full.  When the last block is partly filled and shared,
+ * the sequence moves to a fresh block and (*cow_src, *cow_dst) name the copy
+ * the caller must make (pa_copy_blocks) before storing; otherwise both are
+ * -1. */
+pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq, int32_t* slot,
+                               int32_t* cow_src, int32_t* cow_dst);
+
+/* One decode step for a batch: pa_alloc_append_slot on seqs[0..n) in order.
+ * slots_out: host int32 [n]; cow_pairs_out: host int32 [n][2] receives the
+ * copies in order, their count in *num_cow.  On failure *num_done tells how
+ * many appends succeeded (those stay applied). */
+pa_status pa_alloc_append_batch(pa_allocator* a, const int64_t* seqs, int32_t n,
+                                int32_t* slots_out, int32_t* cow_pairs_out,
+                                int32_t* num_cow, int32_t* num_done);
+
+/* Drop a finished sequence; blocks whose count reaches 0 go back on the list. */
+pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq);
+
+/* Write block tables (host int32 [n][row_stride], padding -1) and context
+ * lengths (host int32 [n], nullable) of seqs[0..n). */
+pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seqs, int32_t n,
+                          int32_t row_stride, int32_t* block_tables_out,
+                          int32_t* context_lens_out);
+
+pa_status pa_alloc_get_stats(const pa_allocator* a, pa_alloc_stats* out);
+
+/* Reference count of a block, or -1 if out of range. */
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);
+
+/* Number of free blocks. */
+int32_t pa_alloc_num_free(const pa_allocator* a);
+
+/* Copy up to `cap` entries of the free list, front first; returns the count
+ * written (for inspection and tests). */
+int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap);
+
+/* Length (tokens) and block count of a sequence. */
+pa_status pa_alloc_seq_info(const pa_allocator* a, int64_t seq,
+                            int32_t* n_tokens, int32_t* n_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,316 @@
+"""Paged KV-cache decode for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of ``lib/libpa.so``: the names match the C ABI in
+``include/pa.h`` and every function only marshals arguments (tensor pointers,
+shapes, the current HIP stream).  All work runs in the library's HIP kernels
+or its C++ allocator; there is no Python or CPU fallback.  Importing the
+package fails loudly when the library has not been built
+(``python -m paged_kv_cache_382_amd.build``).
+
+PyTorch is used only for device memory and streams.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "PaError", "CacheDesc", "lib",
+    "pa_store_kvcache", "pa_copy_blocks", "pa_decode",
+    "pa_decode_workspace_bytes", "pa_decode_partition_tokens",
+    "pa_set_validate", "pa_version", "Allocator",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
+
+STATUS = {
+    0: "OK", 1: "NULL", 2: "SHAPE", 3: "ALIGN", 4: "UNSUPPORTED", 5: "RANGE",
+    6: "WORKSPACE", 7: "OUT_OF_BLOCKS", 8: "SEQ_LIMIT", 9: "UNKNOWN_SEQ",
+    10: "SEQ_EXISTS", 11: "HIP",
+}
+
+
+class PaError(RuntimeError):
+    """A failed library call; ``code`` is the status name (e.g. "OUT_OF_BLOCKS")."""
+
+    def __init__(self, status, message):
+        self.status = int(status)
+        self.code = STATUS.get(self.status, str(status))
+        super().__init__(f"{self.code}: {message}")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class AllocStats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
+                ("cow_copies", ctypes.c_int64), ("live_seqs", ctypes.c_int64),
+                ("logical_tokens", ctypes.c_int64), ("stored_tokens", ctypes.c_int64),
+                ("utilisation", ctypes.c_double), ("internal_fragmentation", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+# name -> (restype, argtypes): every symbol declared in include/pa.h
+SIGNATURES = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_set_validate": (ctypes.c_int, [ctypes.c_int]),
+    "pa_store_kvcache": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, ctypes.POINTER(CacheDesc), _P]),
+    "pa_copy_blocks": (ctypes.c_int, [_P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P]),
+    "pa_decode": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P, _I32, _I32,
+                                 _I32, ctypes.c_float, _P, _I32, _P, ctypes.c_size_t, _P]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32]),
+    "pa_decode_partition_tokens": (_I32, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32]),
+    "pa_alloc_create": (ctypes.c_int, [_I32, _I32, _I32, _PI32, ctypes.POINTER(_P)]),
+    "pa_alloc_destroy": (None, [_P]),
+    "pa_alloc_add_seq": (ctypes.c_int, [_P, _I64, _I32, _PI32]),
+    "pa_alloc_fork": (ctypes.c_int, [_P, _I64, _I64]),
+    "pa_alloc_append_slot": (ctypes.c_int, [_P, _I64, _PI32, _PI32, _PI32]),
+    "pa_alloc_append_batch": (ctypes.c_int, [_P, _PI64, _I32, _PI32, _PI32, _PI32, _PI32]),
+    "pa_alloc_free_seq": (ctypes.c_int, [_P, _I64]),
+    "pa_alloc_export": (ctypes.c_int, [_P, _PI64, _I32, _I32, _PI32, _PI32]),
+    "pa_alloc_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(AllocStats)]),
+    "pa_alloc_refcount": (_I32, [_P, _I32]),
+    "pa_alloc_num_free": (_I32, [_P]),
+    "pa_alloc_free_list": (_I32, [_P, _PI32, _I32]),
+    "pa_alloc_seq_info": (ctypes.c_int, [_P, _I64, _PI32, _PI32]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_382_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+lib()   # fail at import time, not at first call, when the library is missing
+
+
+def _check(status):
+    if status != 0:
+        raise PaError(status, lib().pa_last_error().decode())
+
+
+def pa_version():
+    return lib().pa_version().decode()
+
+
+def pa_set_validate(on):
+    """Turn the library's validation mode on/off; returns the previous setting."""
+    return bool(lib().pa_set_validate(1 if on else 0))
+
+
+# --------------------------------------------------------------------------
+# device calls
+# --------------------------------------------------------------------------
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def cache_desc(k_cache):
+    nb, bs, hkv, d = k_cache.shape
+    return CacheDesc(nb, bs, hkv, d)
+
+
+def pa_store_kvcache(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """Write k/v [N, Hkv, D] fp16 rows to the cache slots in slot_mapping [N] int32."""
+    import torch
+    if k_cache.shape != v_cache.shape or k.shape != v.shape:
+        raise ValueError("k/v and k_cache/v_cache must have matching shapes")
+    desc = cache_desc(k_cache)
+    n = k.shape[0]
+    if k.dim() != 3 or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_dim):
+        raise ValueError("k must be [N, num_kv_heads, head_dim]")
+    if slot_mapping.numel() != n:
+        raise ValueError("slot_mapping must have one entry per token")
+    _check(lib().pa_store_kvcache(
+        _dev(k, torch.float16, "k"), _dev(v, torch.float16, "v"),
+        _dev(slot_mapping, torch.int32, "slot_mapping"), n,
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
+        ctypes.byref(desc), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None):
+    """Copy whole blocks src_dst[i][0] -> src_dst[i][1] in both caches."""
+    import torch
+    desc = cache_desc(k_cache)
+    n = src_dst.shape[0] if src_dst.numel() else 0
+    if src_dst.numel() and (src_dst.dim() != 2 or src_dst.shape[1] != 2):
+        raise ValueError("src_dst must be [n, 2]")
+    _check(lib().pa_copy_blocks(
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
+        ctypes.byref(desc), _dev(src_dst, torch.int32, "src_dst") if n else None, n,
+        _stream(stream)))
+
+
+def pa_decode_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len, partition_tokens=0):
+    return int(lib().pa_decode_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                               max_context_len, partition_tokens))
+
+
+def pa_decode_partition_tokens(desc, num_seqs, num_q_heads, max_context_len, partition_tokens=0):
+    return int(lib().pa_decode_partition_tokens(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                max_context_len, partition_tokens))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+              max_context_len=None, partition_tokens=0, workspace=None, stream=None):
+    """Single-query paged attention; returns ``out`` [B, Hq, D] fp16.
+
+    ``max_context_len`` (host int) bounds ``context_lens``; by default the
+    table width times the block size.  ``workspace`` (a uint8 device tensor)
+    is allocated when needed and not given.
+    """
+    import torch
+    desc = cache_desc(k_cache)
+    B, hq, d = q.shape
+    M = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = M * desc.block_size
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_decode_workspace_bytes(desc, B, hq, max_context_len, partition_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, torch.uint8, "workspace") if need else None
+    ws_bytes = workspace.numel() if need else 0
+    if tuple(block_tables.shape[:1]) != (B,) or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    _check(lib().pa_decode(
+        _dev(q, torch.float16, "q"), _dev(k_cache, torch.float16, "k_cache"),
+        _dev(v_cache, torch.float16, "v_cache"), ctypes.byref(desc),
+        _dev(block_tables, torch.int32, "block_tables"), M,
+        _dev(context_lens, torch.int32, "context_lens"), B, hq, int(max_context_len),
+        float(scale), _dev(out, torch.float16, "out"), int(partition_tokens), ws_ptr, ws_bytes,
+        _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# host allocator
+# --------------------------------------------------------------------------
+
+def _i32p(a):
+    return a.ctypes.data_as(_PI32)
+
+
+class Allocator:
+    """The C++ block manager: FIFO free list, block tables, refcounts, CoW."""
+
+    def __init__(self, num_blocks, block_size, max_blocks_per_seq, initial_free_order=None):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if order.size != self.num_blocks:
+                raise PaError(5, "initial order must list every block")
+        h = ctypes.c_void_p()
+        _check(lib().pa_alloc_create(self.num_blocks, self.block_size, self.max_blocks_per_seq,
+                                     _i32p(order) if order is not None else None, ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.pa_alloc_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq, n_tokens):
+        slots = np.empty(max(int(n_tokens), 1), dtype=np.int32)
+        _check(lib().pa_alloc_add_seq(self._h, int(seq), int(n_tokens), _i32p(slots)))
+        return slots[:int(n_tokens)]
+
+    def fork(self, parent, child):
+        _check(lib().pa_alloc_fork(self._h, int(parent), int(child)))
+
+    def append_slot(self, seq):
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_alloc_append_slot(self._h, int(seq), ctypes.byref(slot),
+                                          ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def append_batch(self, seqs):
+        """One token for each sequence; returns (slots [n], cow pairs [k, 2])."""
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = ids.size
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        n_cow, n_done = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_alloc_append_batch(self._h, ids.ctypes.data_as(_PI64), n, _i32p(slots),
+                                           _i32p(pairs), ctypes.byref(n_cow), ctypes.byref(n_done)))
+        return slots[:n], pairs[:n_cow.value]
+
+    def free_seq(self, seq):
+        _check(lib().pa_alloc_free_seq(self._h, int(seq)))
+
+    def export(self, seqs, row_stride):
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = ids.size
+        tables = np.empty((max(n, 1), int(row_stride)), dtype=np.int32)
+        lens = np.empty(max(n, 1), dtype=np.int32)
+        _check(lib().pa_alloc_export(self._h, ids.ctypes.data_as(_PI64), n, int(row_stride),
+                                     _i32p(tables), _i32p(lens)))
+        return tables[:n], lens[:n]
+
+    def stats(self):
+        st = AllocStats()
+        _check(lib().pa_alloc_get_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in AllocStats._fields_}
+
+    def refcount(self, block):
+        return int(lib().pa_alloc_refcount(self._h, int(block)))
+
+    def num_free(self):
+        return int(lib().pa_alloc_num_free(self._h))
+
+    def free_list(self):
+        out = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        n = lib().pa_alloc_free_list(self._h, _i32p(out), self.num_blocks)
+        return out[:n]
+
+    def seq_info(self, seq):
+        n_tok, n_blk = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_alloc_seq_info(self._h, int(seq), ctypes.byref(n_tok), ctypes.byref(n_blk)))
+        return n_tok.value, n_blk.value
+
+    def seq_len(self, seq):
+        return self.seq_info(seq)[0]

@@ -1,0 +1,299 @@
+// Host-side block manager: FIFO free list, per-sequence block tables,
+// reference counts, fork and copy-on-write.
+//
+// Sources (cited by page title):
+//  * "Deep dive into the nano-vLLM inference engine architecture:
+//    PagedAttention memory management", section "PagedAttention: the
+//    operating system's memory wisdom": a free-block list and a per-sequence
+//    logical-to-physical table; a request receives its first blocks on
+//    arrival and a fresh block whenever its current block fills.
+//  * same page, section "Continuous batching and memory management working
+//    together": a finished request returns all its blocks to the free list.
+//  * "vLLM core architecture: PagedAttention principle, KV Cache management,
+//    continuous batching", section 2 ("KV Cache management"): pages of a
+//    common prefix are shared; a shared page is copied only when a sharer
+//    modifies it; reference counts keep a shared page alive until its last
+//    user is done.
+//
+// Every operation checks everything it needs before mutating anything, so a
+// failed call leaves the state unchanged.
+
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+struct Seq {
+    std::vector<int32_t> blocks;
+    int32_t n_tokens = 0;
+};
+
+// Fixed-capacity ring buffer holding the free list.
+class FreeList {
+public:
+    explicit FreeList(int32_t cap) : buf_(static_cast<size_t>(cap)) {}
+    int32_t size() const { return count_; }
+    bool empty() const { return count_ == 0; }
+    int32_t pop_front() {
+        int32_t b = buf_[head_];
+        head_ = (head_ + 1) % cap();
+        --count_;
+        return b;
+    }
+    void push_back(int32_t b) {
+        buf_[(head_ + count_) % cap()] = b;
+        ++count_;
+    }
+    int32_t at(int32_t i) const { return buf_[(head_ + i) % cap()]; }
+
+private:
+    int32_t cap() const { return static_cast<int32_t>(buf_.size()); }
+    std::vector<int32_t> buf_;
+    int32_t head_ = 0;
+    int32_t count_ = 0;
+};
+
+}  // namespace
+
+struct pa_allocator {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+    FreeList free_list;
+    std::vector<int32_t> refcount;
+    std::unordered_map<int64_t, Seq> seqs;
+    int64_t cow_copies = 0;
+
+    pa_allocator(int32_t nb, int32_t bs, int32_t mb)
+        : num_blocks(nb), block_size(bs), max_blocks_per_seq(mb), free_list(nb),
+          refcount(static_cast<size_t>(nb), 0) {}
+
+    int32_t slot_of(const Seq& s, int32_t pos) const {
+        return s.blocks[pos / block_size] * block_size + pos % block_size;
+    }
+};
+
+using pa::fail;
+using pa::ok;
+
+extern "C" {
+
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                          int32_t max_blocks_per_seq,
+                          const int32_t* initial_free_order, pa_allocator** out) {
+    if (!out) return fail(PA_ERR_NULL, "pa_alloc_create: out is NULL");
+    *out = nullptr;
+    if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
+        return fail(PA_ERR_SHAPE, "pa_alloc_create: sizes must be positive");
+    if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+        return fail(PA_ERR_RANGE, "pa_alloc_create: num_blocks*block_size overflows int32 slots");
+    pa_allocator* a = new (std::nothrow) pa_allocator(num_blocks, block_size, max_blocks_per_seq);
+    if (!a) return fail(PA_ERR_RANGE, "pa_alloc_create: out of host memory");
+    if (initial_free_order) {
+        std::vector<char> seen(static_cast<size_t>(num_blocks), 0);
+        for (int32_t i = 0; i < num_blocks; ++i) {
+            int32_t b = initial_free_order[i];
+            if (b < 0 || b >= num_blocks || seen[b]) {
+                delete a;
+                return fail(PA_ERR_RANGE, "pa_alloc_create: initial order is not a permutation (entry %d)", i);
+            }
+            seen[b] = 1;
+        }
+        for (int32_t i = 0; i < num_blocks; ++i) a->free_list.push_back(initial_free_order[i]);
+    } else {
+        for (int32_t i = 0; i < num_blocks; ++i) a->free_list.push_back(i);
+    }
+    *out = a;
+    return ok();
+}
+
+void pa_alloc_destroy(pa_allocator* a) { delete a; }
+
+pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq, int32_t n_tokens, int32_t* slots_out) {
+    if (!a) return fail(PA_ERR_NULL, "pa_alloc_add_seq: allocator is NULL");
+    if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq: sequence %lld exists", (long long)seq);
+    if (n_tokens < 0) return fail(PA_ERR_RANGE, "pa_alloc_add_seq: negative token count");
+    int32_t need = (n_tokens + a->block_size - 1) / a->block_size;
+    if (need > a->max_blocks_per_seq)
+        return fail(PA_ERR_SEQ_LIMIT, "pa_alloc_add_seq: %d blocks exceed the per-sequence limit %d", need, a->max_blocks_per_seq);
+    if (need > a->free_list.size())
+        return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_add_seq: need %d blocks, %d free", need, a->free_list.size());
+    Seq s;
+    s.blocks.reserve(static_cast<size_t>(need));
+    for (int32_t i = 0; i < need; ++i) {
+        int32_t b = a->free_list.pop_front();
+        a->refcount[b] = 1;
+        s.blocks.push_back(b);
+    }
+    s.n_tokens = n_tokens;
+    if (slots_out)
+        for (int32_t p = 0; p < n_tokens; ++p) slots_out[p] = a->slot_of(s, p);
+    a->seqs.emplace(seq, std::move(s));
+    return ok();
+}
+
+pa_status pa_alloc_fork(pa_allocator* a, int64_t parent, int64_t child) {
+    if (!a) return fail(PA_ERR_NULL, "pa_alloc_fork: allocator is NULL");
+    auto it = a->seqs.find(parent);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_fork: unknown parent %lld", (long long)parent);
+    if (a->seqs.count(child)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_fork: child %lld exists", (long long)child);
+    Seq copy = it->second;
+    for (int32_t b : copy.blocks) ++a->refcount[b];
+    a->seqs.emplace(child, std::move(copy));
+    return ok();
+}
+
+static pa_status append_one(pa_allocator* a, int64_t seq, int32_t* slot, int32_t* src, int32_t* dst) {
+    auto it = a->seqs.find(seq);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_append_slot: unknown sequence %lld", (long long)seq);
+    Seq& s = it->second;
+    const int32_t pos = s.n_tokens;
+    int32_t cs = -1, cd = -1;
+    if (pos % a->block_size == 0) {
+        if (static_cast<int32_t>(s.blocks.size()) >= a->max_blocks_per_seq)
+            return fail(PA_ERR_SEQ_LIMIT, "pa_alloc_append_slot: sequence %lld at its block limit", (long long)seq);
+        if (a->free_list.empty()) return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_append_slot: no free block");
+        int32_t b = a->free_list.pop_front();
+        a->refcount[b] = 1;
+        s.blocks.push_back(b);
+    } else {
+        int32_t last = s.blocks.back();
+        if (a->refcount[last] > 1) {
+            if (a->free_list.empty()) return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_append_slot: no free block for copy-on-write");
+            int32_t fresh = a->free_list.pop_front();
+            --a->refcount[last];
+            a->refcount[fresh] = 1;
+            s.blocks.back() = fresh;
+            cs = last;
+            cd = fresh;
+            ++a->cow_copies;
+        }
+    }
+    s.n_tokens = pos + 1;
+    *slot = a->slot_of(s, pos);
+    *src = cs;
+    *dst = cd;
+    return PA_OK;
+}
+
+pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq, int32_t* slot, int32_t* cow_src, int32_t* cow_dst) {
+    if (!a || !slot || !cow_src || !cow_dst) return fail(PA_ERR_NULL, "pa_alloc_append_slot: NULL argument");
+    pa_status st = append_one(a, seq, slot, cow_src, cow_dst);
+    return st == PA_OK ? ok() : st;
+}
+
+pa_status pa_alloc_append_batch(pa_allocator* a, const int64_t* seqs, int32_t n, int32_t* slots_out,
+                                int32_t* cow_pairs_out, int32_t* num_cow, int32_t* num_done) {
+    if (!a || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !num_cow || !num_done)
+        return fail(PA_ERR_NULL, "pa_alloc_append_batch: NULL argument");
+    if (n < 0) return fail(PA_ERR_SHAPE, "pa_alloc_append_batch: negative count");
+    *num_cow = 0;
+    *num_done = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t src, dst;
+        pa_status st = append_one(a, seqs[i], &slots_out[i], &src, &dst);
+        if (st != PA_OK) return st;
+        if (src >= 0) {
+            cow_pairs_out[2 * *num_cow] = src;
+            cow_pairs_out[2 * *num_cow + 1] = dst;
+            ++*num_cow;
+        }
+        *num_done = i + 1;
+    }
+    return ok();
+}
+
+pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq) {
+    if (!a) return fail(PA_ERR_NULL, "pa_alloc_free_seq: allocator is NULL");
+    auto it = a->seqs.find(seq);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_free_seq: unknown sequence %lld", (long long)seq);
+    for (int32_t b : it->second.blocks)
+        if (--a->refcount[b] == 0) a->free_list.push_back(b);
+    a->seqs.erase(it);
+    return ok();
+}
+
+pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seqs, int32_t n, int32_t row_stride,
+                          int32_t* block_tables_out, int32_t* context_lens_out) {
+    if (!a || (n > 0 && (!seqs || !block_tables_out))) return fail(PA_ERR_NULL, "pa_alloc_export: NULL argument");
+    if (n < 0 || row_stride <= 0) return fail(PA_ERR_SHAPE, "pa_alloc_export: bad sizes");
+    for (int32_t i = 0; i < n; ++i) {          // check everything first
+        auto it = a->seqs.find(seqs[i]);
+        if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_export: unknown sequence %lld", (long long)seqs[i]);
+        if (static_cast<int32_t>(it->second.blocks.size()) > row_stride)
+            return fail(PA_ERR_SHAPE, "pa_alloc_export: sequence %lld has %zu blocks > row stride %d",
+                        (long long)seqs[i], it->second.blocks.size(), row_stride);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq& s = a->seqs.find(seqs[i])->second;
+        int32_t* row = block_tables_out + static_cast<size_t>(i) * row_stride;
+        std::copy(s.blocks.begin(), s.blocks.end(), row);
+        std::fill(row + s.blocks.size(), row + row_stride, -1);
+        if (context_lens_out) context_lens_out[i] = s.n_tokens;
+    }
+    return ok();
+}
+
+pa_status pa_alloc_get_stats(const pa_allocator* a, pa_alloc_stats* out) {
+    if (!a || !out) return fail(PA_ERR_NULL, "pa_alloc_get_stats: NULL argument");
+    std::vector<int32_t> fill(static_cast<size_t>(a->num_blocks), 0);
+    int64_t logical = 0;
+    for (const auto& kv : a->seqs) {
+        const Seq& s = kv.second;
+        logical += s.n_tokens;
+        for (size_t j = 0; j < s.blocks.size(); ++j) {
+            int64_t in_block = static_cast<int64_t>(s.n_tokens) - static_cast<int64_t>(j) * a->block_size;
+            int32_t f = static_cast<int32_t>(std::min<int64_t>(a->block_size, in_block));
+            fill[s.blocks[j]] = std::max(fill[s.blocks[j]], f);
+        }
+    }
+    int32_t used = 0, shared = 0;
+    int64_t filled = 0;
+    for (int32_t b = 0; b < a->num_blocks; ++b) {
+        if (a->refcount[b] > 0) ++used;
+        if (a->refcount[b] > 1) ++shared;
+        filled += fill[b];
+    }
+    out->num_blocks = a->num_blocks;
+    out->free_blocks = a->free_list.size();
+    out->used_blocks = used;
+    out->shared_blocks = shared;
+    out->cow_copies = a->cow_copies;
+    out->live_seqs = static_cast<int64_t>(a->seqs.size());
+    out->logical_tokens = logical;
+    out->stored_tokens = filled;
+    out->utilisation = static_cast<double>(used) / a->num_blocks;
+    const double slots = static_cast<double>(used) * a->block_size;
+    out->internal_fragmentation = used ? (slots - static_cast<double>(filled)) / slots : 0.0;
+    return ok();
+}
+
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block) {
+    if (!a || block < 0 || block >= a->num_blocks) return -1;
+    return a->refcount[block];
+}
+
+int32_t pa_alloc_num_free(const pa_allocator* a) { return a ? a->free_list.size() : 0; }
+
+int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap) {
+    if (!a || !out || cap <= 0) return 0;
+    int32_t n = std::min(cap, a->free_list.size());
+    for (int32_t i = 0; i < n; ++i) out[i] = a->free_list.at(i);
+    return n;
+}
+
+pa_status pa_alloc_seq_info(const pa_allocator* a, int64_t seq, int32_t* n_tokens, int32_t* n_blocks) {
+    if (!a || !n_tokens || !n_blocks) return fail(PA_ERR_NULL, "pa_alloc_seq_info: NULL argument");
+    auto it = a->seqs.find(seq);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_seq_info: unknown sequence %lld", (long long)seq);
+    *n_tokens = it->second.n_tokens;
+    *n_blocks = static_cast<int32_t>(it->second.blocks.size());
+    return ok();
+}
+
+}  // extern "C"

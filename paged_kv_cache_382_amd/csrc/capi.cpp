@@ -1,0 +1,300 @@
+// C ABI of the device calls: argument checks, optional deep validation of the
+// integer metadata, workspace sizing and kernel dispatch.  Every check runs
+// before any launch, so a failing call enqueues nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace pa {
+
+std::string& error_text() {
+    static thread_local std::string text;
+    return text;
+}
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int32_t kMinAutoPartition = 256;
+constexpr int32_t kMaxPartition = 4096;
+constexpr int64_t kTargetWorkgroups = 1024;
+// The merge kernel keeps one fp32 weight per partition in LDS (64 KiB cap).
+constexpr int32_t kMaxPartitions = 16384;
+
+int validate_from_env() {
+    const char* e = std::getenv("PA_VALIDATE");
+    return (e && e[0] == '1') ? 1 : 0;
+}
+
+int& validate_flag() {
+    static int flag = validate_from_env();
+    return flag;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status check_cache(const pa_cache_desc* c, const char* fn) {
+    if (!c) return fail(PA_ERR_NULL, "%s: cache descriptor is NULL", fn);
+    if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
+        return fail(PA_ERR_SHAPE, "%s: cache sizes must be positive", fn);
+    if (static_cast<int64_t>(c->num_blocks) * c->block_size > INT32_MAX)
+        return fail(PA_ERR_RANGE, "%s: num_blocks * block_size exceeds the int32 slot range", fn);
+    return PA_OK;
+}
+
+// Copy `n` int32 values from device memory to the host (validation mode only).
+pa_status fetch(const int32_t* dev, size_t n, std::vector<int32_t>& host, hipStream_t stream,
+                const char* fn) {
+    host.resize(n);
+    if (n == 0) return PA_OK;
+    hipError_t err = hipMemcpyAsync(host.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (err == hipSuccess) err = hipStreamSynchronize(stream);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: validation copy failed: %s", fn, hipGetErrorString(err));
+    return PA_OK;
+}
+
+int32_t resolve_partition(const pa_cache_desc* c, int32_t num_seqs, int32_t max_context_len,
+                          int32_t requested) {
+    if (requested != 0) return requested;
+    // Enough (sequence, partition, KV head) workgroups to fill 256 CUs, with
+    // partitions long enough that the split-K merge stays a small fraction.
+    const int64_t items = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads;
+    int64_t parts = (kTargetWorkgroups + items - 1) / items;
+    if (parts < 1) parts = 1;
+    int64_t t = (static_cast<int64_t>(max_context_len) + parts - 1) / parts;
+    t = (t + 15) / 16 * 16;
+    if (t < kMinAutoPartition) t = kMinAutoPartition;
+    if (t > kMaxPartition) t = kMaxPartition;
+    return static_cast<int32_t>(t);
+}
+
+int32_t num_partitions(int32_t max_context_len, int32_t t) {
+    const int64_t p = (static_cast<int64_t>(max_context_len) + t - 1) / t;
+    return p < 1 ? 1 : static_cast<int32_t>(p);
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout: part_ml fp32 [B][Hq][P][2], then part_o fp32 [B][Hq][P][D].
+size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t parts) {
+    if (parts <= 1) return 0;
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * parts;
+    return round_up(rows * 2 * sizeof(float)) + round_up(rows * head_dim * sizeof(float));
+}
+
+pa_status check_decode_shapes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_context_len, int32_t partition_tokens, const char* fn) {
+    pa_status st = check_cache(c, fn);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0)
+        return fail(PA_ERR_SHAPE, "%s: num_seqs, num_q_heads and max_context_len must be >= 0 / > 0", fn);
+    if (num_q_heads % c->num_kv_heads != 0)
+        return fail(PA_ERR_SHAPE, "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
+                    num_q_heads, c->num_kv_heads);
+    if (!decode_supported(c->head_dim, c->block_size, num_q_heads / c->num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d, block_size %d, group %d not supported", fn,
+                    c->head_dim, c->block_size, num_q_heads / c->num_kv_heads);
+    if (partition_tokens != 0 &&
+        (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16 != 0))
+        return fail(PA_ERR_RANGE, "%s: partition_tokens must be 0 or a multiple of 16 in [16, %d]", fn,
+                    kMaxPartition);
+    return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+using pa::fail;
+using pa::ok;
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa::error_text().c_str(); }
+
+const char* pa_version(void) { return "0.1.0"; }
+
+int pa_set_validate(int on) {
+    int prev = pa::validate_flag();
+    pa::validate_flag() = on ? 1 : 0;
+    return prev;
+}
+
+pa_status pa_store_kvcache(const void* k, const void* v, const int32_t* slot_mapping,
+                           int32_t num_tokens, void* k_cache, void* v_cache,
+                           const pa_cache_desc* cache, void* hip_stream) {
+    static const char* fn = "pa_store_kvcache";
+    pa_status st = pa::check_cache(cache, fn);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0) return fail(PA_ERR_SHAPE, "%s: negative num_tokens", fn);
+    if (cache->head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8", fn);
+    if (num_tokens == 0) return ok();
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+    if (!pa::aligned16(k) || !pa::aligned16(v) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache))
+        return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
+    const int64_t total_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
+    const int64_t row_vec16 = static_cast<int64_t>(cache->num_kv_heads) * cache->head_dim / 8;
+    if (row_vec16 > INT32_MAX / 2) return fail(PA_ERR_SHAPE, "%s: row too large", fn);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (pa::validate_flag()) {
+        std::vector<int32_t> slots;
+        st = pa::fetch(slot_mapping, static_cast<size_t>(num_tokens), slots, stream, fn);
+        if (st != PA_OK) return st;
+        std::unordered_set<int32_t> seen;
+        for (int32_t t = 0; t < num_tokens; ++t) {
+            int32_t s = slots[t];
+            if (s < 0) continue;
+            if (s >= total_slots) return fail(PA_ERR_RANGE, "%s: slot %d of token %d out of range", fn, s, t);
+            if (!seen.insert(s).second) return fail(PA_ERR_RANGE, "%s: slot %d written twice", fn, s);
+        }
+    }
+    hipError_t err = pa::launch_store_kvcache(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                              static_cast<int32_t>(row_vec16), total_slots, stream);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return ok();
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cache,
+                         const int32_t* src_dst, int32_t num_pairs, void* hip_stream) {
+    static const char* fn = "pa_copy_blocks";
+    pa_status st = pa::check_cache(cache, fn);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0) return fail(PA_ERR_SHAPE, "%s: negative num_pairs", fn);
+    if (cache->head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8", fn);
+    if (num_pairs == 0) return ok();
+    if (!k_cache || !v_cache || !src_dst) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+    if (!pa::aligned16(k_cache) || !pa::aligned16(v_cache))
+        return fail(PA_ERR_ALIGN, "%s: caches must be 16-byte aligned", fn);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (pa::validate_flag()) {
+        std::vector<int32_t> pairs;
+        st = pa::fetch(src_dst, static_cast<size_t>(num_pairs) * 2, pairs, stream, fn);
+        if (st != PA_OK) return st;
+        std::unordered_set<int32_t> dsts, srcs;
+        for (int32_t i = 0; i < num_pairs; ++i) {
+            int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+            if (s < 0 || s >= cache->num_blocks || d < 0 || d >= cache->num_blocks)
+                return fail(PA_ERR_RANGE, "%s: pair %d (%d, %d) out of range", fn, i, s, d);
+            if (!dsts.insert(d).second) return fail(PA_ERR_RANGE, "%s: destination %d repeated", fn, d);
+            srcs.insert(s);
+        }
+        for (int32_t d : dsts)
+            if (srcs.count(d)) return fail(PA_ERR_RANGE, "%s: block %d is both source and destination", fn, d);
+    }
+    const int64_t block_vec16 = static_cast<int64_t>(cache->block_size) * cache->num_kv_heads * cache->head_dim / 8;
+    hipError_t err = pa::launch_copy_blocks(k_cache, v_cache, src_dst, num_pairs, block_vec16,
+                                            cache->num_blocks, stream);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return ok();
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t partition_tokens) {
+    if (pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len, partition_tokens,
+                                "pa_decode_workspace_bytes") != PA_OK)
+        return 0;
+    const int32_t t = pa::resolve_partition(cache, num_seqs, max_context_len, partition_tokens);
+    return pa::workspace_for(num_seqs, num_q_heads, cache->head_dim,
+                             pa::num_partitions(max_context_len, t));
+}
+
+int32_t pa_decode_partition_tokens(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_context_len, int32_t partition_tokens) {
+    if (pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len, partition_tokens,
+                                "pa_decode_partition_tokens") != PA_OK)
+        return 0;
+    return pa::resolve_partition(cache, num_seqs, max_context_len, partition_tokens);
+}
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const pa_cache_desc* cache, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* hip_stream) {
+    static const char* fn = "pa_decode";
+    pa_status st = pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len,
+                                           partition_tokens, fn);
+    if (st != PA_OK) return st;
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
+    if (num_seqs == 0) return ok();
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+    if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
+        return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
+    const int32_t t = pa::resolve_partition(cache, num_seqs, max_context_len, partition_tokens);
+    const int32_t parts = pa::num_partitions(max_context_len, t);
+    const size_t need = pa::workspace_for(num_seqs, num_q_heads, cache->head_dim, parts);
+    if (need > 0) {
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+        if (workspace_bytes < need)
+            return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % pa::kAlign != 0)
+            return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+    }
+    if (parts > pa::kMaxPartitions)
+        return fail(PA_ERR_RANGE, "%s: %d partitions exceed the limit %d (raise partition_tokens)", fn,
+                    parts, pa::kMaxPartitions);
+    const int64_t grid = static_cast<int64_t>(num_seqs) * parts * cache->num_kv_heads;
+    if (grid > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld workgroups)", fn, (long long)grid);
+    const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
+                                                   max_context_len);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (pa::validate_flag()) {
+        std::vector<int32_t> lens, tables;
+        st = pa::fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
+        if (st != PA_OK) return st;
+        st = pa::fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
+        if (st != PA_OK) return st;
+        for (int32_t s = 0; s < num_seqs; ++s) {
+            const int32_t L = lens[s];
+            if (L < 0 || L > max_tokens64)
+                return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [0, %lld]", fn, s, L,
+                            (long long)max_tokens64);
+            const int32_t used = (L + cache->block_size - 1) / cache->block_size;
+            for (int32_t j = 0; j < used; ++j) {
+                const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
+                if (b < 0 || b >= cache->num_blocks)
+                    return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
+            }
+        }
+    }
+    pa::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = static_cast<uint16_t*>(out);
+    if (need > 0) {
+        const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * parts;
+        a.part_ml = static_cast<float*>(workspace);
+        a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pa::round_up(rows * 2 * sizeof(float)));
+    }
+    a.num_blocks = cache->num_blocks;
+    a.block_size = cache->block_size;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.head_dim = cache->head_dim;
+    a.num_q_heads = num_q_heads;
+    a.num_seqs = num_seqs;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_tokens = static_cast<int32_t>(max_tokens64);
+    a.partition_tokens = t;
+    a.max_parts = parts;
+    a.scale_log2 = scale * pa::kLog2e;
+    hipError_t err = pa::launch_decode(a, stream);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal launch interface between the C ABI (capi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pa {
+
+// Arguments of one paged decode call, already checked by the caller.
+struct DecodeArgs {
+    const uint16_t* q;             // fp16 [B][Hq][D]
+    const uint16_t* k_cache;       // fp16 [NB][BS][Hkv][D]
+    const uint16_t* v_cache;
+    const int32_t* block_tables;   // [B][M]
+    const int32_t* context_lens;   // [B]
+    uint16_t* out;                 // fp16 [B][Hq][D]
+    float* part_o;                 // fp32 [B][Hq][P][D]     (P > 1 only)
+    float* part_ml;                // fp32 [B][Hq][P][2]     (running max, sum)
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t num_q_heads;
+    int32_t num_seqs;
+    int32_t max_blocks_per_seq;    // M, row stride of block_tables
+    int32_t max_tokens;            // clamp of context lengths
+    int32_t partition_tokens;      // T
+    int32_t max_parts;             // P = ceil(max_context_len / T), >= 1
+    float scale_log2;              // scale * log2(e)
+};
+
+bool decode_supported(int head_dim, int block_size, int group);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_store_kvcache(const void* k, const void* v, const int32_t* slots,
+                                int32_t num_tokens, void* k_cache, void* v_cache,
+                                int32_t row_vec16, int64_t total_slots, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                              int32_t num_pairs, int64_t block_vec16, int32_t num_blocks,
+                              hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,53 @@
+"""The benchmark's traffic model against the pages' closed forms."""
+
+import json
+import os
+
+import pytest
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_kv_bytes_per_request_is_about_1gb():
+    g = golden("kv_bytes_per_request.json")
+    n = bench.kv_bytes_per_request(g["layers"], g["hidden"], g["tokens"], g["bytes_per_element"])
+    assert n == 1 << 30                                   # exactly 1 GiB
+    assert abs(n - g["approx_bytes"]) / g["approx_bytes"] <= g["approx_rel_tolerance"]
+
+
+def test_128k_context_table_entries():
+    g = golden("blocks_128k.json")
+    # one table entry (4 bytes) per block of the context
+    lens = [g["context_tokens"]]
+    kv = g["context_tokens"] * 1 * 128 * 2 * 2
+    n = bench.decode_bytes(lens, 1, 1, 128, g["block_size"])
+    assert n - kv - 2 * 128 * 2 - 4 == g["blocks"] * 4
+
+
+@pytest.mark.parametrize("lens,hq,hkv,bs,expect", [
+    ([2048] * 32, 32, 32, 16, 1_074_282_624),            # bs32 ctx2048 MHA
+    ([131072] * 4, 32, 8, 16, 2_147_680_272),            # 4 x 128K GQA, block 16
+    ([131072] * 4, 32, 8, 8, 2_147_811_344),             # block 8
+    ([131072] * 4, 32, 8, 64, 2_147_581_968),            # block 64
+])
+def test_decode_bytes_worked_values(lens, hq, hkv, bs, expect):
+    assert bench.decode_bytes(lens, hq, hkv, 128, bs) == expect
+
+
+def test_table_overhead_below_one_percent():
+    """Mapping-table memory stays under 1% of the KV cache it maps."""
+    for hkv, bs in [(8, 8), (8, 16), (32, 16), (8, 64)]:
+        per_block_kv = bs * hkv * 128 * 2 * 2
+        assert 4 / per_block_kv < 0.01
+
+
+def test_store_and_copy_bytes():
+    assert bench.store_bytes(32, 32, 128) == 4 * 32 * 32 * 128 * 2 + 128
+    assert bench.copy_bytes(1, 16, 8, 128) == 4 * 16 * 8 * 128 * 2
