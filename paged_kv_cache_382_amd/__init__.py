@@ -92,6 +92,10 @@ def lib():
     """The loaded library (loaded on first use)."""
     global _lib
     if _lib is None:
+        # PyTorch ships its own HIP runtime under another file name.  Loading
+        # it first makes libpa.so bind to that same runtime (matched by
+        # soname) instead of pulling a second copy into the process.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_382_amd.build`")

@@ -383,7 +383,9 @@ void decode_partition_kernel(const DecodeArgs a) {
             den = __builtin_fmaf(f, s_l[w][h], den);
         }
         if (nparts == 1) {
-            const float r = den > 0.f ? num / den : 0.f;
+            // den is 0 only when no token was read (e.g. every table entry of
+            // the partition was out of range); NaN inputs still propagate.
+            const float r = den == 0.f ? 0.f : num / den;
             const _Float16 hv = static_cast<_Float16>(r);
             a.out[out_row0 + o] = __builtin_bit_cast(uint16_t, hv);
         } else {
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
     uint16_t* out = a.out + static_cast<size_t>(sh) * D + lane * PER_LANE;
 #pragma unroll
     for (int e = 0; e < PER_LANE; ++e) {
-        const float r = den > 0.f ? acc[e] / den : 0.f;
+        const float r = den == 0.f ? 0.f : acc[e] / den;
         out[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
     }
 }

@@ -165,6 +165,7 @@ def test_single_token_context_returns_value_row_exactly():
 
 def test_empty_context_gives_zero_rows():
     p = build(MEDIUM, plan_fn=medium_plan())
+    run_step(p, partition_tokens=256)         # caches now hold the step's tokens
     lens = p["lens"].clone()
     lens[2] = 0
     out = torch.full_like(p["q"], float("nan"))
@@ -173,7 +174,7 @@ def test_empty_context_gives_zero_rows():
                  max_context_len=p["max_ctx"], partition_tokens=256)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out[2]).item() == 0
-    kc, vc = p["ref"]["pre_k"], p["ref"]["pre_v"]
+    kc, vc = oracle_caches(p)
     r = p["ref"]
     ref = decode_ref(r["q"], kc.view(np.float16), vc.view(np.float16), r["tables"],
                      lens.cpu().numpy(), MEDIUM.scale)
