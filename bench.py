@@ -2,7 +2,7 @@
 
 A step is the whole hot path for one batch, over every layer: copy-on-write
 block copies (when the allocator asked for any), the store of the step's new
-K/V rows, and paged decode attention (partition kernel + split-K merge).  The
+K/V rows, and paged decode attention (balanced split kernel + merge).  The
 block tables, slot mapping and context lengths come from the library's C++
 allocator; its per-step host cost is timed separately (``host_step_us``) since
 it runs on the CPU ahead of the GPU work.
@@ -166,16 +166,50 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s):
     }
 
 
+def copy_probe(wl, dev, reps):
+    """Copy blocks [0, NB/2) onto [NB/2, NB) in both caches, ``reps`` times.
+
+    Each launch reads and writes exactly ``copy_bytes(NB/2, ...) / 2`` bytes;
+    the HBM byte counters of this launch calibrate those of the decode kernel.
+    """
+    import torch
+
+    import paged_kv_cache_382_amd as pa
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    kc = torch.zeros(shape, dtype=torch.float16, device=dev)
+    vc = torch.zeros_like(kc)
+    half = wl.num_blocks // 2
+    pairs = torch.stack([torch.arange(half), torch.arange(half) + half], 1).to(
+        device=dev, dtype=torch.int32).contiguous()
+    n = copy_bytes(half, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    pa.pa_copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        pa.pa_copy_blocks(kc, vc, pairs)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    print(json.dumps({"copy_probe": wl.name, "read_bytes": n // 2, "write_bytes": n // 2,
+                      "launches": reps + 1, "us_per_launch": round(ms * 1e3, 3),
+                      "gbps_read_plus_write": round(n / (ms * 1e-3) / 1e9, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mha")
-    ap.add_argument("--partition", type=int, default=0, help="split-K tokens (0 = library choice)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="pieces the decode work is cut into (0 = library default)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run pa_copy_blocks over half the pool of one layer (a plain copy "
+                         "of known size, for scaling the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only; --gpus must be 1 (multi-GPU runs are not "
@@ -190,6 +224,9 @@ def main():
     layers = args.layers or wl.layers
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(wl, dev, max(args.steps, 1))
+        return
 
     alloc = pa.Allocator(wl.num_blocks, wl.block_size, wl.max_blocks_per_seq,
                          W.free_order(wl.num_blocks, wl.seed))
@@ -220,9 +257,8 @@ def main():
     cows = torch.tensor([list(c) for c in plan.cow_pairs], dtype=torch.int32,
                         device=dev).reshape(-1, 2)
     desc = pa.CacheDesc(*shape)
-    T = pa.pa_decode_partition_tokens(desc, B, hq, max_ctx, args.partition)
-    ws_bytes = pa.pa_decode_workspace_bytes(desc, B, hq, max_ctx, args.partition)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    splits = pa.pa_decode_num_splits(desc, hq, args.splits)
+    ws = pa.decode_workspace(desc, B, hq, splits, dev)
 
     def step(events=None):
         for layer in range(layers):
@@ -233,7 +269,7 @@ def main():
             if events is not None:
                 events[layer][0].record()
             pa.pa_decode(q[layer], kc, vc, tables, lens_d, wl.scale, out=out[layer],
-                         max_context_len=max_ctx, partition_tokens=T, workspace=ws)
+                         max_context_len=max_ctx, num_splits=splits, workspace=ws)
             if events is not None:
                 events[layer][1].record()
 
@@ -275,7 +311,7 @@ def main():
             "workload": describe(wl, plan),
             "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
             "context_min": min(lens), "context_max": max_ctx, "context_sum": sum(lens),
-            "layers": layers, "partition_tokens": T, "pool_blocks": wl.num_blocks,
+            "layers": layers, "num_splits": splits, "pool_blocks": wl.num_blocks,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
@@ -283,7 +319,7 @@ def main():
         "decode_us_per_layer": round(dec_avg_ms * 1e3, 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (partition kernel + split-K merge when it runs)",
+            "kernel": "pa_decode (balanced split kernel + merge kernel)",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

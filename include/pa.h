@@ -145,41 +145,51 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  *   context_lens   device int32 [num_seqs]; each must be at most
  *                  max_context_len and at most max_blocks_per_seq*block_size
  *                  (larger values are clamped; rejected in validation mode).
- *   max_context_len  host upper bound of context_lens; sizes the launch.
+ *   max_context_len  host upper bound of context_lens (longer contexts are
+ *                  clamped to it; rejected in validation mode).
  *   scale          softmax scale (commonly 1/sqrt(head_dim)).
  *   out            device fp16 [num_seqs][num_q_heads][head_dim] (written)
- *   partition_tokens  tokens per split-K partition; 0 picks one from the
- *                  shapes.  Must be 0 or a multiple of 16 in [16, 4096].
+ *   num_splits     number of equal pieces N the work is cut into, one
+ *                  workgroup each; 0 picks as many as the current device
+ *                  holds at once.  The 16-token chunks of all (sequence, KV
+ *                  head) pairs, in sequence-major order, are divided into N
+ *                  contiguous ranges.  A pair that straddles ranges gets
+ *                  fp32 partials (running max, sum, weighted values) from
+ *                  each, which a second kernel combines, in range order, into
+ *                  the output (online-softmax merge).  Must be in [0, 2^20].
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes with the same shape arguments, 256-byte aligned; may
- *                  be NULL when that size is 0.  Its contents on entry do not
- *                  matter.
+ *                  bytes (same cache, num_seqs, num_q_heads, num_splits, on
+ *                  the same device), 256-byte aligned, for those partials.
+ *                  Its contents on entry do not matter; calls sharing a
+ *                  workspace must not overlap.
  *
  * Supported: head_dim 64 or 128; block_size 8, 16, 32 or 64; num_q_heads a
  * multiple of num_kv_heads with a group size of 1, 2, 4 or 8.  Other shapes
- * return PA_ERR_UNSUPPORTED.  Results depend only on logical token order, not
- * on which physical blocks hold the tokens: moving blocks (and rewriting the
- * tables to match) gives bitwise identical output.
+ * return PA_ERR_UNSUPPORTED.  Results depend only on the context lengths and
+ * N, never on which physical blocks hold the tokens or on which workgroup
+ * handled which range: moving blocks (and rewriting the tables to match)
+ * gives bitwise identical output.
  */
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const pa_cache_desc* cache,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t max_context_len, float scale,
-                    void* out, int32_t partition_tokens,
+                    void* out, int32_t num_splits,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Bytes of workspace pa_decode needs for these shapes (0 when every sequence
- * fits one partition).  Returns 0 for unsupported or invalid shapes too. */
+/* Bytes of workspace pa_decode needs: (N + num_seqs * num_kv_heads) slots of
+ * G x (head_dim + 2) floats, with G = num_q_heads / num_kv_heads and N the
+ * resolved num_splits, each of the two arrays rounded up to 256 bytes.
+ * Returns 0 for unsupported or invalid shapes. */
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
-                                 int32_t num_q_heads, int32_t max_context_len,
-                                 int32_t partition_tokens);
+                                 int32_t num_q_heads, int32_t num_splits);
 
-/* The partition size pa_decode uses for these shapes (resolves 0 = auto).
- * Returns 0 for invalid shapes. */
-int32_t pa_decode_partition_tokens(const pa_cache_desc* cache, int32_t num_seqs,
-                                   int32_t num_q_heads, int32_t max_context_len,
-                                   int32_t partition_tokens);
+/* The number of splits N pa_decode uses (resolves 0 from the current
+ * device's occupancy, assuming 1024 resident workgroups when no device can be
+ * queried).  Returns 0 for invalid shapes. */
+int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads,
+                             int32_t num_splits);
 
 /* ----------------------------------------------------------------------- */
 /* Host-side block allocator (the block manager).

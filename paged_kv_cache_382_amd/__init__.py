@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "PaError", "CacheDesc", "lib",
     "pa_store_kvcache", "pa_copy_blocks", "pa_decode",
-    "pa_decode_workspace_bytes", "pa_decode_partition_tokens",
+    "pa_decode_workspace_bytes", "pa_decode_num_splits",
     "pa_set_validate", "pa_version", "Allocator",
 ]
 
@@ -68,8 +68,8 @@ SIGNATURES = {
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P]),
     "pa_decode": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P, _I32, _I32,
                                  _I32, ctypes.c_float, _P, _I32, _P, ctypes.c_size_t, _P]),
-    "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32]),
-    "pa_decode_partition_tokens": (_I32, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32]),
+    "pa_decode_num_splits": (_I32, [ctypes.POINTER(CacheDesc), _I32, _I32]),
     "pa_alloc_create": (ctypes.c_int, [_I32, _I32, _I32, _PI32, ctypes.POINTER(_P)]),
     "pa_alloc_destroy": (None, [_P]),
     "pa_alloc_add_seq": (ctypes.c_int, [_P, _I64, _I32, _PI32]),
@@ -184,23 +184,31 @@ def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None):
         _stream(stream)))
 
 
-def pa_decode_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len, partition_tokens=0):
+def pa_decode_workspace_bytes(desc, num_seqs, num_q_heads, num_splits=0):
     return int(lib().pa_decode_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
-                                               max_context_len, partition_tokens))
+                                               num_splits))
 
 
-def pa_decode_partition_tokens(desc, num_seqs, num_q_heads, max_context_len, partition_tokens=0):
-    return int(lib().pa_decode_partition_tokens(ctypes.byref(desc), num_seqs, num_q_heads,
-                                                max_context_len, partition_tokens))
+def pa_decode_num_splits(desc, num_q_heads, num_splits=0):
+    return int(lib().pa_decode_num_splits(ctypes.byref(desc), num_q_heads, num_splits))
+
+
+def decode_workspace(desc, num_seqs, num_q_heads, num_splits=0, device="cuda"):
+    """A workspace for pa_decode with these shapes (contents irrelevant)."""
+    import torch
+    n = pa_decode_workspace_bytes(desc, num_seqs, num_q_heads, num_splits)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
-              max_context_len=None, partition_tokens=0, workspace=None, stream=None):
+              max_context_len=None, num_splits=0, workspace=None, stream=None):
     """Single-query paged attention; returns ``out`` [B, Hq, D] fp16.
 
     ``max_context_len`` (host int) bounds ``context_lens``; by default the
-    table width times the block size.  ``workspace`` (a uint8 device tensor)
-    is allocated when needed and not given.
+    table width times the block size.  ``num_splits`` is the number of equal
+    pieces (one workgroup each) the work is cut into (0: as many workgroups as
+    the GPU holds at once).  ``workspace`` (a uint8 device tensor from
+    ``decode_workspace``) is allocated when not given.
     """
     import torch
     desc = cache_desc(k_cache)
@@ -210,19 +218,19 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         max_context_len = M * desc.block_size
     if out is None:
         out = torch.empty_like(q)
-    need = pa_decode_workspace_bytes(desc, B, hq, max_context_len, partition_tokens)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, torch.uint8, "workspace") if need else None
-    ws_bytes = workspace.numel() if need else 0
     if tuple(block_tables.shape[:1]) != (B,) or context_lens.numel() != B:
         raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    need = pa_decode_workspace_bytes(desc, B, hq, num_splits) if B else 0
+    if need and workspace is None:
+        workspace = decode_workspace(desc, B, hq, num_splits, q.device)
+    ws_ptr = _dev(workspace, torch.uint8, "workspace") if need else None
+    ws_bytes = workspace.numel() if need else 0
     _check(lib().pa_decode(
         _dev(q, torch.float16, "q"), _dev(k_cache, torch.float16, "k_cache"),
         _dev(v_cache, torch.float16, "v_cache"), ctypes.byref(desc),
         _dev(block_tables, torch.int32, "block_tables"), M,
         _dev(context_lens, torch.int32, "context_lens"), B, hq, int(max_context_len),
-        float(scale), _dev(out, torch.float16, "out"), int(partition_tokens), ws_ptr, ws_bytes,
+        float(scale), _dev(out, torch.float16, "out"), int(num_splits), ws_ptr, ws_bytes,
         _stream(stream)))
     return out
 

@@ -25,11 +25,9 @@ std::string& error_text() {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int32_t kMinAutoPartition = 256;
-constexpr int32_t kMaxPartition = 4096;
-constexpr int64_t kTargetWorkgroups = 1024;
-// The merge kernel keeps one fp32 weight per partition in LDS (64 KiB cap).
-constexpr int32_t kMaxPartitions = 16384;
+// Workgroups assumed resident when the device cannot be queried (no GPU).
+constexpr int32_t kFallbackResident = 1024;
+constexpr int32_t kMaxSplits = 1 << 20;
 
 int validate_from_env() {
     const char* e = std::getenv("PA_VALIDATE");
@@ -63,38 +61,36 @@ pa_status fetch(const int32_t* dev, size_t n, std::vector<int32_t>& host, hipStr
     return PA_OK;
 }
 
-int32_t resolve_partition(const pa_cache_desc* c, int32_t num_seqs, int32_t max_context_len,
-                          int32_t requested) {
-    if (requested != 0) return requested;
-    // Enough (sequence, partition, KV head) workgroups to fill 256 CUs, with
-    // partitions long enough that the split-K merge stays a small fraction.
-    const int64_t items = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads;
-    int64_t parts = (kTargetWorkgroups + items - 1) / items;
-    if (parts < 1) parts = 1;
-    int64_t t = (static_cast<int64_t>(max_context_len) + parts - 1) / parts;
-    t = (t + 15) / 16 * 16;
-    if (t < kMinAutoPartition) t = kMinAutoPartition;
-    if (t > kMaxPartition) t = kMaxPartition;
-    return static_cast<int32_t>(t);
+int32_t resident_workgroups(const pa_cache_desc* c, int32_t num_q_heads) {
+    const int r = decode_resident_workgroups(c->head_dim, c->block_size, num_q_heads / c->num_kv_heads);
+    return r > 0 ? r : kFallbackResident;
 }
 
-int32_t num_partitions(int32_t max_context_len, int32_t t) {
-    const int64_t p = (static_cast<int64_t>(max_context_len) + t - 1) / t;
-    return p < 1 ? 1 : static_cast<int32_t>(p);
+// Default split count: one per workgroup the device holds at once, so the
+// whole grid runs in a single round.
+int32_t resolve_splits(const pa_cache_desc* c, int32_t num_q_heads, int32_t requested) {
+    if (requested > 0) return requested;
+    return std::min<int32_t>(resident_workgroups(c, num_q_heads), kMaxSplits);
 }
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: part_ml fp32 [B][Hq][P][2], then part_o fp32 [B][Hq][P][D].
-size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t parts) {
-    if (parts <= 1) return 0;
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * parts;
-    return round_up(rows * 2 * sizeof(float)) + round_up(rows * head_dim * sizeof(float));
+// Partial-result slots: one per split plus one per (sequence, KV head).
+size_t partial_rows(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads, int32_t splits) {
+    const size_t slots = static_cast<size_t>(splits) + static_cast<size_t>(num_seqs) * c->num_kv_heads;
+    return slots * static_cast<size_t>(num_q_heads / c->num_kv_heads);
+}
+
+// Workspace layout: part_ml fp32 [slots][G][2], then part_o fp32
+// [slots][G][D], each 256-byte aligned.
+size_t workspace_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads, int32_t splits) {
+    const size_t rows = partial_rows(c, num_seqs, num_q_heads, splits);
+    return round_up(rows * 2 * sizeof(float)) + round_up(rows * c->head_dim * sizeof(float));
 }
 
 pa_status check_decode_shapes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
-                              int32_t max_context_len, int32_t partition_tokens, const char* fn) {
+                              int32_t max_context_len, int32_t num_splits, const char* fn) {
     pa_status st = check_cache(c, fn);
     if (st != PA_OK) return st;
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0)
@@ -105,10 +101,8 @@ pa_status check_decode_shapes(const pa_cache_desc* c, int32_t num_seqs, int32_t 
     if (!decode_supported(c->head_dim, c->block_size, num_q_heads / c->num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d, block_size %d, group %d not supported", fn,
                     c->head_dim, c->block_size, num_q_heads / c->num_kv_heads);
-    if (partition_tokens != 0 &&
-        (partition_tokens < 16 || partition_tokens > kMaxPartition || partition_tokens % 16 != 0))
-        return fail(PA_ERR_RANGE, "%s: partition_tokens must be 0 or a multiple of 16 in [16, %d]", fn,
-                    kMaxPartition);
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return fail(PA_ERR_RANGE, "%s: num_splits must be in [0, %d]", fn, kMaxSplits);
     return PA_OK;
 }
 
@@ -199,32 +193,29 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
 }
 
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t max_context_len, int32_t partition_tokens) {
-    if (pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len, partition_tokens,
+                                 int32_t num_splits) {
+    if (pa::check_decode_shapes(cache, num_seqs, num_q_heads, 0, num_splits,
                                 "pa_decode_workspace_bytes") != PA_OK)
         return 0;
-    const int32_t t = pa::resolve_partition(cache, num_seqs, max_context_len, partition_tokens);
-    return pa::workspace_for(num_seqs, num_q_heads, cache->head_dim,
-                             pa::num_partitions(max_context_len, t));
+    return pa::workspace_for(cache, num_seqs, num_q_heads,
+                             pa::resolve_splits(cache, num_q_heads, num_splits));
 }
 
-int32_t pa_decode_partition_tokens(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
-                                   int32_t max_context_len, int32_t partition_tokens) {
-    if (pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len, partition_tokens,
-                                "pa_decode_partition_tokens") != PA_OK)
+int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads, int32_t num_splits) {
+    if (pa::check_decode_shapes(cache, 1, num_q_heads, 0, num_splits, "pa_decode_num_splits") != PA_OK)
         return 0;
-    return pa::resolve_partition(cache, num_seqs, max_context_len, partition_tokens);
+    return pa::resolve_splits(cache, num_q_heads, num_splits);
 }
 
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const pa_cache_desc* cache, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
-                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    int32_t num_splits, void* workspace, size_t workspace_bytes,
                     void* hip_stream) {
     static const char* fn = "pa_decode";
     pa_status st = pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len,
-                                           partition_tokens, fn);
+                                           num_splits, fn);
     if (st != PA_OK) return st;
     if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
     if (num_seqs == 0) return ok();
@@ -232,21 +223,15 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
         return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
     if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
         return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
-    const int32_t t = pa::resolve_partition(cache, num_seqs, max_context_len, partition_tokens);
-    const int32_t parts = pa::num_partitions(max_context_len, t);
-    const size_t need = pa::workspace_for(num_seqs, num_q_heads, cache->head_dim, parts);
-    if (need > 0) {
-        if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
-        if (workspace_bytes < need)
-            return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
-        if (reinterpret_cast<uintptr_t>(workspace) % pa::kAlign != 0)
-            return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-    }
-    if (parts > pa::kMaxPartitions)
-        return fail(PA_ERR_RANGE, "%s: %d partitions exceed the limit %d (raise partition_tokens)", fn,
-                    parts, pa::kMaxPartitions);
-    const int64_t grid = static_cast<int64_t>(num_seqs) * parts * cache->num_kv_heads;
-    if (grid > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld workgroups)", fn, (long long)grid);
+    const int32_t splits = pa::resolve_splits(cache, num_q_heads, num_splits);
+    const size_t need = pa::workspace_for(cache, num_seqs, num_q_heads, splits);
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+    if (workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % pa::kAlign != 0)
+        return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+    const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
+    if (pairs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld pairs)", fn, (long long)pairs);
     const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
                                                    max_context_len);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -276,10 +261,11 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.out = static_cast<uint16_t*>(out);
-    if (need > 0) {
-        const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * parts;
-        a.part_ml = static_cast<float*>(workspace);
-        a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pa::round_up(rows * 2 * sizeof(float)));
+    {
+        const size_t rows = pa::partial_rows(cache, num_seqs, num_q_heads, splits);
+        char* ws = static_cast<char*>(workspace);
+        a.part_ml = reinterpret_cast<float*>(ws);
+        a.part_o = reinterpret_cast<float*>(ws + pa::round_up(rows * 2 * sizeof(float)));
     }
     a.num_blocks = cache->num_blocks;
     a.block_size = cache->block_size;
@@ -289,8 +275,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     a.num_seqs = num_seqs;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_tokens = static_cast<int32_t>(max_tokens64);
-    a.partition_tokens = t;
-    a.max_parts = parts;
+    a.num_splits = splits;
     a.scale_log2 = scale * pa::kLog2e;
     hipError_t err = pa::launch_decode(a, stream);
     if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));

@@ -12,40 +12,50 @@
 //  * "Deep analysis of nano-vLLM's paged KV cache and memory optimisation
 //    architecture", section "Engineering: configuration and monitoring":
 //    decode attention reads the paged cache directly (plain attention being
-//    the fallback), and section 3 of the vLLM page ties decode speed to
-//    memory bandwidth.
+//    the fallback); section 3 of the vLLM page ties decode speed to memory
+//    bandwidth.
 //
 // What is computed, per sequence s and query head h (KV head g = h / G):
 //   out[s][h] = sum_p softmax_p(scale * q[s][h] . K[s,p,g]) V[s,p,g]
 // with K/V row p found in physical block table[s][p / BS], row p % BS.
 //
-// Design (HBM-bound streaming, no matrix cores: G <= 8 query rows never fill
+// Design (HBM-bound streaming; no matrix cores: G <= 8 query rows never fill
 // an MFMA tile):
-//  * Work item = (sequence, split-K partition of T tokens, KV head); one
-//    workgroup of 4 wave64s per item.  The G query heads sharing the KV head
+//  * Balanced split.  The work is the list of 16-token chunks of every
+//    (sequence, KV head) pair, in sequence-major order; the grid is W
+//    workgroups (by default as many as the device holds at once) and
+//    workgroup w takes the contiguous range [w*U/W, (w+1)*U/W) of the U
+//    chunks.  Every workgroup streams the same number of bytes, whatever the
+//    mix of context lengths, and the whole grid starts in one round.  A
+//    range crosses pair boundaries: each piece of it (a "segment") is one
+//    pair's chunks [c0, c1).
+//  * A segment that covers a whole pair is normalised and written to fp16
+//    directly.  Otherwise the workgroup writes fp32 (m, l, o) partials to
+//    slot w + pair of the workspace (distinct for every segment: along the
+//    chunk order, either w or pair grows at each segment start), and the merge
+//    kernel combines the slots of workgroups first(pair) .. last(pair).
+//  * Within a segment, chunks are dealt round-robin to the 4 wave64s of the
+//    workgroup.  A K (or V) row of D fp16 is D/8 lanes x 16 bytes, so one
+//    buffer_load_dwordx4 per lane covers 64/(D/8) whole rows (1 KiB per wave
+//    instruction, fully coalesced).  The G query heads sharing the KV head
 //    live in registers, so every K/V byte is fetched from HBM once.
-//  * Within a partition, 16-token chunks are dealt round-robin to the 4
-//    waves.  A K (or V) row of D fp16 is D/8 lanes x 16 bytes, so one
-//    global_load_dwordx4 per lane covers 64/(D/8) whole rows (1 KiB per wave
-//    instruction, fully coalesced).
-//  * Block numbers: each wave loads the table entries of its own chunks into
-//    one VGPR (lane k <- chunk k) at the start and reads them back with
-//    v_readlane into SGPRs, so the per-load address is a 64-bit scalar base
+//  * Block numbers: a wave loads the table entries of up to 64 of its chunks
+//    into one VGPR (lane k <- chunk k) and reads them back with v_readlane
+//    into SGPRs, so each load is a scalar buffer base (the physical block)
 //    plus a per-lane constant offset.  No LDS round trip, no barrier.
 //  * Software pipelining: the next chunk's K and V loads are issued before
-//    the current chunk is consumed (two register buffers).
+//    the current chunk is consumed (two register buffers).  The loads carry
+//    the non-temporal hint: every byte is read once per call.
 //  * Each 16-lane row group keeps its own online-softmax stream (running max
 //    m, sum l, fp32 accumulator of its 8 columns), so the per-chunk work
 //    needs only an in-row DPP butterfly for the q.k dot product; the row
-//    groups, then the 4 waves (through LDS), are merged once at the end.
+//    groups, then the 4 waves (through LDS), are merged once per segment.
 //  * Exponentials are exp2 with scale*log2(e) folded into the scores.
-//  * Partitions of a sequence beyond the first write fp32 (m, l, o) partials;
-//    a reduction kernel merges them.  A sequence that fits one partition is
-//    written straight to fp16 by the partition kernel.
-//  * Every reduction has a fixed order that depends only on logical token
-//    positions, so results are bitwise reproducible and independent of
-//    which physical blocks hold the tokens.
+//  * The split depends only on the context lengths and W, and every
+//    reduction has a fixed order, so results are bitwise reproducible and
+//    independent of which physical blocks hold the tokens.
 
+#include <atomic>
 #include <type_traits>
 
 #include "kernels.h"
@@ -59,14 +69,18 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kChunk = 16;         // tokens per chunk
-// Occupancy the register allocator may trade down to while keeping two
-// 16-token chunks of K and V in flight per wave: 4 waves per SIMD (128 VGPRs)
-// for 1-2 query heads per KV head, 3 (168) for 4, 2 (256) for 8.
+// Occupancy (waves per SIMD) the register allocator may trade down to while
+// keeping two chunks of K and V in registers: 4 waves (128 VGPRs) for 1-2
+// query heads per KV head, 3 (168) for 4, 2 (256) for 8.
 template <int G>
-constexpr int min_waves_per_simd() { return G <= 2 ? 4 : (G == 4 ? 3 : 2); }
+constexpr int waves_per_simd() { return G <= 2 ? 4 : (G == 4 ? 3 : 2); }
 constexpr float kNegBig = -1.0e30f;  // start value of a running max
 // Word 3 of a gfx9-family buffer resource: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: the "nt" (non-temporal) bit.  Every
+// K/V byte is read once per call, so the loads are marked as streaming; on
+// gfx950 this raises sustained read bandwidth by about a tenth.
+constexpr int kNonTemporal = 2;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -94,6 +108,56 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, kWave); }
 
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int64_t y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Wave-uniform value of lane `src` (src itself uniform), in scalar registers.
+__device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), src);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32), src);
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) { return readlane64(x, 0); }
+
+// Context length of sequence s, clamped to [0, max_tokens].
+__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int s) {
+    const int L = a.context_lens[s];
+    return L < 0 ? 0 : (L > a.max_tokens ? a.max_tokens : L);
+}
+
+__device__ __forceinline__ int chunks_of(int L) { return (L + kChunk - 1) / kChunk; }
+
+// Chunks of one KV head over the whole batch (wave-uniform result).
+__device__ int64_t chunks_per_head(const DecodeArgs& a, int lane) {
+    int64_t tot = 0;
+    for (int b0 = 0; b0 < a.num_seqs; b0 += kWave) {
+        const int s = b0 + lane;
+        tot += wave_sum64(s < a.num_seqs ? chunks_of(clamped_len(a, s)) : 0);
+    }
+    return uniform64(tot);
+}
+
+// The split whose range holds chunk x: the largest w with floor(w*U/W) <= x,
+// i.e. floor(((x+1)*W - 1) / U).
+__device__ __forceinline__ int owner_of(int64_t x, int64_t U, int W) {
+    return static_cast<int>(((x + 1) * W - 1) / U);
+}
+
 template <int D>
 struct Geometry {
     static constexpr int LPR = D / 8;            // lanes per token row
@@ -101,21 +165,15 @@ struct Geometry {
     static constexpr int LPC = kChunk / RPL;     // loads per chunk (K or V)
 };
 
-template <int LPC>
-struct Frag {
-    uint4 k[LPC];
-    uint4 v[LPC];
-    uint32_t row_ok;   // bit i: this lane's row of load i holds a real token
-};
-
 template <int D, int BS, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<G>())))
-void decode_partition_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<G>())))
+void decode_split_kernel(const DecodeArgs a) {
     using Geo = Geometry<D>;
     constexpr int LPR = Geo::LPR;
     constexpr int RPL = Geo::RPL;
     constexpr int LPC = Geo::LPC;
     constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;   // blocks per chunk
+    constexpr int kPerBlock = LPC / BPC;                  // granules of a chunk per block
     static_assert(BS % RPL == 0, "a load must not straddle two blocks");
 
     __shared__ float s_acc[kWaves][G][D];
@@ -123,350 +181,511 @@ void decode_partition_kernel(const DecodeArgs a) {
     __shared__ float s_l[kWaves][G];
 
     const int lane = threadIdx.x & (kWave - 1);
-    // threadIdx.x / 64 is the same in every lane of a wave; readfirstlane
-    // tells the compiler so, which keeps all chunk bookkeeping in SGPRs.
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wave = uniform(threadIdx.x / kWave);
     const int row = lane / LPR;
     const int col = lane % LPR;
+    const int Hkv = a.num_kv_heads;
+    const int N = a.num_splits;
 
-    int item = blockIdx.x;
-    const int g = item % a.num_kv_heads;
-    item /= a.num_kv_heads;
-    const int part = item % a.max_parts;
-    const int s = item / a.max_parts;
-
-    const int T = a.partition_tokens;
-    int L = a.context_lens[s];
-    L = L < 0 ? 0 : (L > a.max_tokens ? a.max_tokens : L);
-    const int nparts = (L + T - 1) / T;
-    const int h0 = g * G;
-    const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
-
-    if (part >= nparts) {
-        if (L == 0 && part == 0) {       // empty context: zero output rows
-            for (int i = threadIdx.x; i < G * D; i += kThreads) a.out[out_row0 + i] = 0;
-        }
-        return;
-    }
-
-    const int t_begin = part * T;
-    const int len = (L - t_begin < T) ? (L - t_begin) : T;
-    const int n_chunks = (len + kChunk - 1) / kChunk;
-    const int n_local = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
-
-    // Table entries of this wave's chunks: lane k holds chunk k's blocks.
-    int ids[BPC];
-    bool bad = false;
-    {
-        const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
-        const int c = wave + lane * kWaves;
-        const int j0 = (t_begin + c * kChunk) / BS;
-#pragma unroll
-        for (int e = 0; e < BPC; ++e) {
-            int id = -1;
-            const int j = j0 + e;
-            if (lane < n_local && j * BS < L) {
-                id = trow[j];
-                if (id < 0 || id >= a.num_blocks) {
-                    id = -1;
-                    bad = true;
-                }
-            }
-            ids[e] = id;
-        }
-    }
-    const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-
-    // This lane's 8 columns of the G query rows.
-    half2_t qv[G][4];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const uint4 w = *reinterpret_cast<const uint4*>(a.q + out_row0 + h * D + col * 8);
-        qv[h][0] = __builtin_bit_cast(half2_t, w.x);
-        qv[h][1] = __builtin_bit_cast(half2_t, w.y);
-        qv[h][2] = __builtin_bit_cast(half2_t, w.z);
-        qv[h][3] = __builtin_bit_cast(half2_t, w.w);
-    }
-
-    const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;   // one slot
+    const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;   // one slot
     const uint32_t block_bytes = row_bytes * BS;
     // Per-lane byte offset inside a load: row `row` of the load, 16-byte column `col`.
     const uint32_t lane_off = row * row_bytes + col * 16;
-    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + static_cast<size_t>(g) * D * 2;
-    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + static_cast<size_t>(g) * D * 2;
 
-    float m[G], l[G], acc[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = kNegBig;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    }
+    const int64_t U = chunks_per_head(a, lane) * Hkv;
 
-    // Issue the K and V loads of local chunk k (uniform).  Each load goes
-    // through a buffer descriptor whose base is the physical block (scalar),
-    // with this lane's constant 32-bit offset in a VGPR and the row of the
-    // block in an SGPR.  In the masked variant, rows holding no token (ragged
-    // tail, bad table entry) still load from a legal address (block 0 stands
-    // in for a bad entry) and are dropped in compute(), so issuing never
-    // waits for data.
-    auto issue = [&](Frag<LPC>& f, int k, auto masked_tag) {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-        const int c = wave + k * kWaves;
-        const uint32_t tok0 = static_cast<uint32_t>(t_begin + c * kChunk);
-        const int nvalid = len - c * kChunk;            // may exceed 16
-        f.row_ok = 0;
-#pragma unroll
-        for (int e = 0; e < BPC; ++e) {
-            int blk = __builtin_amdgcn_readlane(ids[e], k);
-            const bool blk_ok = blk >= 0;
-            if (kMasked) blk = blk_ok ? blk : 0;
-            const size_t boff = static_cast<size_t>(blk) * block_bytes;
-            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<char*>(kbase + boff), 0, block_bytes, kRsrcWord3);
-            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<char*>(vbase + boff), 0, block_bytes, kRsrcWord3);
-            constexpr int kPerBlock = LPC / BPC;        // loads of this chunk in block e
-#pragma unroll
-            for (int u = 0; u < kPerBlock; ++u) {
-                const int i = e * kPerBlock + u;
-                const uint32_t in_blk = (tok0 + i * RPL) % BS;
-                const int soff = static_cast<int>(in_blk * row_bytes);
-                f.k[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(kr, lane_off, soff, 0));
-                f.v[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(vr, lane_off, soff, 0));
-                if (kMasked) {
-                    const bool ok = blk_ok && (i * RPL + row < nvalid);
-                    f.row_ok |= ok ? (1u << i) : 0u;
+    // Process the chunks [start, end) of split `unit`: walk the pairs they
+    // cover; each piece of a pair (a segment) is reduced by the workgroup and
+    // written as fp16 output (whole pair) or as partials (slot unit + pair).
+    auto process_split = [&](int unit, int64_t start, int64_t end) {
+        // Locate the pair holding chunk `start`: the first sequence whose running
+        // chunk total (times Hkv) passes it.
+        int s = 0, L = 0, nch = 0;
+        int64_t seq_base = 0;        // Hkv * chunks of all earlier sequences
+        {
+            int64_t base = 0;
+            for (int b0 = 0; b0 < a.num_seqs; b0 += kWave) {
+                const int sl = b0 + lane;
+                const int Ll = sl < a.num_seqs ? clamped_len(a, sl) : 0;
+                const int64_t n = chunks_of(Ll);
+                const int64_t incl = wave_incl_scan64(n, lane);
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(sl < a.num_seqs && (base + incl) * Hkv > start);
+                if (hit) {
+                    const int f = __builtin_ctzll(hit);
+                    s = b0 + f;
+                    L = __builtin_amdgcn_readlane(Ll, f);
+                    nch = chunks_of(L);
+                    seq_base = (base + readlane64(incl, f) - nch) * Hkv;
+                    break;
                 }
+                base += readlane64(incl, kWave - 1);
             }
         }
-    };
+        if (nch == 0) return;        // not reached: chunk `start` < U lies in some pair
+        int g = static_cast<int>((start - seq_base) / nch);
+        int c0 = static_cast<int>((start - seq_base) % nch);
+        int64_t pos = start;
 
-    auto compute = [&](const Frag<LPC>& f, auto masked_tag) {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-        float sc[LPC][G];
-#pragma unroll
-        for (int i = 0; i < LPC; ++i) {
-            const half2_t k0 = __builtin_bit_cast(half2_t, f.k[i].x);
-            const half2_t k1 = __builtin_bit_cast(half2_t, f.k[i].y);
-            const half2_t k2 = __builtin_bit_cast(half2_t, f.k[i].z);
-            const half2_t k3 = __builtin_bit_cast(half2_t, f.k[i].w);
-#pragma unroll
+        for (;;) {
+            const int c1 = static_cast<int>(nch - c0 < end - pos ? nch : c0 + (end - pos));
+            const int n_seg = c1 - c0;
+            // This wave's chunks of the segment: c0 + wave + 4k, k < n_local;
+            // the first n_full of them hold 16 tokens each.
+            const int n_local = n_seg > wave ? (n_seg - wave + kWaves - 1) / kWaves : 0;
+            const int full_seg = (c1 * kChunk <= L ? c1 : c1 - 1) - c0;
+            const int n_full = full_seg > wave ? (full_seg - wave + kWaves - 1) / kWaves : 0;
+            const int h0 = g * G;
+            const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
+            const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
+            const char* kbase = reinterpret_cast<const char*>(a.k_cache) + static_cast<size_t>(g) * D * 2;
+            const char* vbase = reinterpret_cast<const char*>(a.v_cache) + static_cast<size_t>(g) * D * 2;
+
+            // This lane's 8 columns of the G query rows.
+            half2_t qv[G][4];
+    #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float d = __builtin_amdgcn_fdot2(qv[h][0], k0, 0.f, false);
-                d = __builtin_amdgcn_fdot2(qv[h][1], k1, d, false);
-                d = __builtin_amdgcn_fdot2(qv[h][2], k2, d, false);
-                d = __builtin_amdgcn_fdot2(qv[h][3], k3, d, false);
-                d = row_sum<LPR>(d) * a.scale_log2;
-                if (kMasked && !((f.row_ok >> i) & 1u)) d = -__builtin_inff();
-                sc[i][h] = d;
+                const uint4 qw = *reinterpret_cast<const uint4*>(a.q + out_row0 + h * D + col * 8);
+                qv[h][0] = __builtin_bit_cast(half2_t, qw.x);
+                qv[h][1] = __builtin_bit_cast(half2_t, qw.y);
+                qv[h][2] = __builtin_bit_cast(half2_t, qw.z);
+                qv[h][3] = __builtin_bit_cast(half2_t, qw.w);
             }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mx = sc[0][h];
-#pragma unroll
-            for (int i = 1; i < LPC; ++i) mx = __builtin_fmaxf(mx, sc[i][h]);
-            const float m_new = __builtin_fmaxf(m[h], mx);
-            const float alpha = fast_exp2(m[h] - m_new);
-            m[h] = m_new;
-            l[h] *= alpha;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-#pragma unroll
-            for (int i = 0; i < LPC; ++i) {
-                const float pr = fast_exp2(sc[i][h] - m_new);
-                l[h] += pr;
-                uint32_t vw[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
-                if (kMasked && !((f.row_ok >> i) & 1u)) {
-                    // p is 0 here, but 0 * (NaN or Inf) is not: drop the row.
-                    vw[0] = vw[1] = vw[2] = vw[3] = 0;
+
+            float m[G], l[G], acc[G][8];
+    #pragma unroll
+            for (int h = 0; h < G; ++h) {
+                m[h] = kNegBig;
+                l[h] = 0.f;
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+            }
+
+            for (int kw = 0; kw < n_local; kw += kWave) {
+                // Table entries of this window of the wave's chunks: lane k holds
+                // local chunk kw + k.
+                int ids[BPC];
+                bool bad = false;
+                {
+                    const int c = c0 + wave + (kw + lane) * kWaves;
+                    const int j0 = c * kChunk / BS;
+    #pragma unroll
+                    for (int e = 0; e < BPC; ++e) {
+                        int id = -1;
+                        const int j = j0 + e;
+                        if (kw + lane < n_local && j * BS < L) {
+                            id = trow[j];
+                            if (id < 0 || id >= a.num_blocks) {
+                                id = -1;
+                                bad = true;
+                            }
+                        }
+                        ids[e] = id;
+                    }
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half2_t v2 = __builtin_bit_cast(half2_t, vw[j]);
-                    acc[h][2 * j] = __builtin_fmaf(pr, static_cast<float>(v2.x), acc[h][2 * j]);
-                    acc[h][2 * j + 1] = __builtin_fmaf(pr, static_cast<float>(v2.y), acc[h][2 * j + 1]);
+                const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+                const int nw = n_local - kw < kWave ? n_local - kw : kWave;          // chunks in window
+                const int nfw = n_full - kw < 0 ? 0 : (n_full - kw < nw ? n_full - kw : nw);
+
+                // Block and in-block row offset of granule i (static, 0 <= i <
+                // LPC: RPL token rows, one per row group) of window chunk k.
+                // A load through a descriptor with an empty range returns zeros
+                // without touching memory: used past the end of the work (so a
+                // pipeline issues the same loads every step and its wait counts
+                // are compile-time constants) and for bad table entries.
+                struct Src {
+                    __amdgpu_buffer_rsrc_t kr, vr;
+                    int soff;
+                    bool ok;          // this lane's row holds a token of the context
+                };
+                auto source = [&](int k, int i, bool live) -> Src {
+                    const int e = i / kPerBlock;
+                    const int c = c0 + wave + (kw + k) * kWaves;
+                    int blk = __builtin_amdgcn_readlane(ids[e], k & (kWave - 1));
+                    const bool blk_ok = blk >= 0;
+                    blk = blk_ok ? blk : 0;
+                    const uint32_t range = (live && blk_ok) ? block_bytes : 0u;
+                    const size_t boff = static_cast<size_t>(blk) * block_bytes;
+                    Src r;
+                    r.kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + boff), 0, range, kRsrcWord3);
+                    r.vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + boff), 0, range, kRsrcWord3);
+                    r.soff = static_cast<int>((static_cast<uint32_t>(c * kChunk + i * RPL) % BS) * row_bytes);
+                    r.ok = blk_ok && (i * RPL + row < L - c * kChunk);
+                    return r;
+                };
+                // Loads are issued in program order (a scheduling barrier after
+                // each): the wait counts of the pipeline depend on the order of
+                // the loads in flight being the same on every path into a step.
+                auto load = [&](const __amdgpu_buffer_rsrc_t& rs, int soff) {
+                    const uint4 r = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, soff, kNonTemporal));
+                    __builtin_amdgcn_sched_barrier(0);
+                    return r;
+                };
+                // Issue a chunk's loads: its K rows first, then its V rows.
+                auto issue_chunk = [&](uint4 (&kd)[LPC], uint4 (&vd)[LPC], int k, bool live) {
+    #pragma unroll
+                    for (int i = 0; i < LPC; ++i) {
+                        const Src r = source(k, i, live);
+                        kd[i] = load(r.kr, r.soff);
+                    }
+    #pragma unroll
+                    for (int i = 0; i < LPC; ++i) {
+                        const Src r = source(k, i, live);
+                        vd[i] = load(r.vr, r.soff);
+                    }
+                };
+
+                // Consume chunk k held in (kd, vd) and refill the registers with
+                // chunk k2 as they free up: the K rows right after the scores,
+                // each V row right after its P.V update.  While a chunk is
+                // consumed, the next chunk and part of the one after are in
+                // flight.  One max update (and rescale) per chunk and row group.
+                auto consume = [&](uint4 (&kd)[LPC], uint4 (&vd)[LPC], int k, int k2, bool live2,
+                                   auto masked_tag) {
+                    constexpr bool kMasked = decltype(masked_tag)::value;
+                    bool ok[LPC];
+                    if (kMasked) {
+    #pragma unroll
+                        for (int i = 0; i < LPC; ++i) ok[i] = source(k, i, true).ok;
+                    }
+                    float sc[LPC][G];
+    #pragma unroll
+                    for (int i = 0; i < LPC; ++i) {
+                        const half2_t k0 = __builtin_bit_cast(half2_t, kd[i].x);
+                        const half2_t k1 = __builtin_bit_cast(half2_t, kd[i].y);
+                        const half2_t k2h = __builtin_bit_cast(half2_t, kd[i].z);
+                        const half2_t k3 = __builtin_bit_cast(half2_t, kd[i].w);
+    #pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            float d = __builtin_amdgcn_fdot2(qv[h][0], k0, 0.f, false);
+                            d = __builtin_amdgcn_fdot2(qv[h][1], k1, d, false);
+                            d = __builtin_amdgcn_fdot2(qv[h][2], k2h, d, false);
+                            d = __builtin_amdgcn_fdot2(qv[h][3], k3, d, false);
+                            d = row_sum<LPR>(d) * a.scale_log2;
+                            if (kMasked && !ok[i]) d = -__builtin_inff();
+                            sc[i][h] = d;
+                        }
+                    }
+                    if (!kMasked) {
+    #pragma unroll
+                        for (int i = 0; i < LPC; ++i) {
+                            const Src r = source(k2, i, live2);
+                            kd[i] = load(r.kr, r.soff);
+                        }
+                    }
+    #pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        float mx = sc[0][h];
+    #pragma unroll
+                        for (int i = 1; i < LPC; ++i) mx = __builtin_fmaxf(mx, sc[i][h]);
+                        const float m_new = __builtin_fmaxf(m[h], mx);
+                        const float alpha = fast_exp2(m[h] - m_new);
+                        m[h] = m_new;
+                        l[h] *= alpha;
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+                    }
+    #pragma unroll
+                    for (int i = 0; i < LPC; ++i) {
+                        uint32_t vw[4] = {vd[i].x, vd[i].y, vd[i].z, vd[i].w};
+                        if (kMasked && !ok[i]) {
+                            // p is 0 here, but 0 * (NaN or Inf) is not: drop the row.
+                            vw[0] = vw[1] = vw[2] = vw[3] = 0;
+                        }
+    #pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            const float pr = fast_exp2(sc[i][h] - m[h]);
+                            l[h] += pr;
+    #pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const half2_t v2 = __builtin_bit_cast(half2_t, vw[j]);
+                                acc[h][2 * j] = __builtin_fmaf(pr, static_cast<float>(v2.x), acc[h][2 * j]);
+                                acc[h][2 * j + 1] = __builtin_fmaf(pr, static_cast<float>(v2.y), acc[h][2 * j + 1]);
+                            }
+                        }
+                        if (!kMasked) {
+                            const Src r = source(k2, i, live2);
+                            vd[i] = load(r.vr, r.soff);
+                        }
+                    }
+                };
+
+                using Full = std::integral_constant<bool, false>;
+                using Masked = std::integral_constant<bool, true>;
+                if (!any_bad && nfw > 0) {
+                    // Chunks alternate between two register sets X and Y.  Both
+                    // loop bodies are unconditional, so every wait is static.
+                    uint4 xk[LPC], xv[LPC], yk[LPC], yv[LPC];
+                    issue_chunk(xk, xv, 0, true);
+                    issue_chunk(yk, yv, 1, 1 < nfw);
+                    int k = 0;
+                    for (; k + 1 < nfw; k += 2) {
+                        consume(xk, xv, k, k + 2, k + 2 < nfw, Full{});
+                        consume(yk, yv, k + 1, k + 3, k + 3 < nfw, Full{});
+                    }
+                    if (k < nfw) consume(xk, xv, k, k + 2, false, Full{});
                 }
+                // The pair's ragged last chunk, or every chunk of a window with a
+                // bad table entry: rows holding no token are dropped.
+                for (int k = any_bad ? 0 : nfw; k < nw; ++k) {
+                    uint4 tk[LPC], tv[LPC];
+                    issue_chunk(tk, tv, k, true);
+                    consume(tk, tv, k, 0, false, Masked{});
+                }
+            }
+
+            // Merge the row groups of this wave (each kept its own stream).
+    #pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float mw = m[h];
+    #pragma unroll
+                for (int o = LPR; o < kWave; o <<= 1) mw = __builtin_fmaxf(mw, shfl_xor(mw, o));
+                const float f = fast_exp2(m[h] - mw);
+                float lw = l[h] * f;
+    #pragma unroll
+                for (int o = LPR; o < kWave; o <<= 1) lw += shfl_xor(lw, o);
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float x = acc[h][e] * f;
+    #pragma unroll
+                    for (int o = LPR; o < kWave; o <<= 1) x += shfl_xor(x, o);
+                    acc[h][e] = x;
+                }
+                m[h] = mw;
+                l[h] = lw;
+            }
+            if (row == 0) {
+    #pragma unroll
+                for (int h = 0; h < G; ++h)
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e) s_acc[wave][h][col * 8 + e] = acc[h][e];
+            }
+            if (lane == 0) {
+    #pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    s_m[wave][h] = m[h];
+                    s_l[wave][h] = l[h];
+                }
+            }
+            __syncthreads();
+
+            // Merge the 4 waves; write the fp16 rows when the segment is the whole
+            // pair, else this segment's partials.
+            const bool whole = c0 == 0 && c1 == nch;
+            const size_t slot = static_cast<size_t>(unit) + static_cast<size_t>(s) * Hkv + g;
+            for (int o = threadIdx.x; o < G * D; o += kThreads) {
+                const int h = o / D;
+                const int d = o % D;
+                float mm = s_m[0][h];
+    #pragma unroll
+                for (int v = 1; v < kWaves; ++v) mm = __builtin_fmaxf(mm, s_m[v][h]);
+                float num = 0.f, den = 0.f;
+    #pragma unroll
+                for (int v = 0; v < kWaves; ++v) {
+                    const float f = fast_exp2(s_m[v][h] - mm);
+                    num = __builtin_fmaf(f, s_acc[v][h][d], num);
+                    den = __builtin_fmaf(f, s_l[v][h], den);
+                }
+                if (whole) {
+                    // den is 0 only when no token was read (every table entry of
+                    // the pair out of range); NaN inputs still propagate.
+                    const float r = den == 0.f ? 0.f : num / den;
+                    a.out[out_row0 + o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
+                } else {
+                    a.part_o[(slot * G + h) * D + d] = num;
+                    if (d == 0) {
+                        a.part_ml[(slot * G + h) * 2] = mm;
+                        a.part_ml[(slot * G + h) * 2 + 1] = den;
+                    }
+                }
+            }
+
+            pos += n_seg;
+            if (pos >= end) break;
+            __syncthreads();             // LDS is reused by the next segment
+            // Next pair: the next KV head, or the next sequence holding tokens.
+            c0 = 0;
+            if (++g == Hkv) {
+                g = 0;
+                L = 0;
+                while (L == 0 && s + 1 < a.num_seqs) L = clamped_len(a, ++s);
+                nch = chunks_of(L);
+                if (nch == 0) break;     // not reached while pos < end
             }
         }
     };
 
-    using Full = std::integral_constant<bool, false>;
-    using Masked = std::integral_constant<bool, true>;
-    // Chunks this wave owns that are completely inside the context; at most
-    // one more (the partition's ragged tail) follows them.
-    const int full_chunks = len / kChunk;
-    const int n_full = full_chunks > wave ? (full_chunks - wave + kWaves - 1) / kWaves : 0;
-    if (!any_bad) {
-        if (n_full > 0) {
-            Frag<LPC> fa, fb;
-            issue(fa, 0, Full{});
-            for (int k = 0; k < n_full; k += 2) {
-                // The prefetch never runs past the last full chunk: at the
-                // end it re-reads that chunk (an L2 hit), so every iteration
-                // issues the same loads and the wait counts stay static.
-                // The scheduling barriers keep the compiler from sinking the
-                // prefetch next to its use, which would serialise latency.
-                const int k1 = k + 1 < n_full ? k + 1 : n_full - 1;
-                issue(fb, k1, Full{});
-                __builtin_amdgcn_sched_barrier(0);
-                compute(fa, Full{});
-                if (k + 1 >= n_full) break;
-                const int k2 = k + 2 < n_full ? k + 2 : n_full - 1;
-                issue(fa, k2, Full{});
-                __builtin_amdgcn_sched_barrier(0);
-                compute(fb, Full{});
-            }
-        }
-        if (n_local > n_full) {
-            Frag<LPC> ft;
-            issue(ft, n_full, Masked{});
-            compute(ft, Masked{});
-        }
-    } else {
-        for (int k = 0; k < n_local; ++k) {
-            Frag<LPC> ft;
-            issue(ft, k, Masked{});
-            compute(ft, Masked{});
-        }
-    }
-
-    // Merge the row groups of this wave (each kept its own stream).
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float mw = m[h];
-#pragma unroll
-        for (int o = LPR; o < kWave; o <<= 1) mw = __builtin_fmaxf(mw, shfl_xor(mw, o));
-        const float f = fast_exp2(m[h] - mw);
-        float lw = l[h] * f;
-#pragma unroll
-        for (int o = LPR; o < kWave; o <<= 1) lw += shfl_xor(lw, o);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[h][e] * f;
-#pragma unroll
-            for (int o = LPR; o < kWave; o <<= 1) x += shfl_xor(x, o);
-            acc[h][e] = x;
-        }
-        m[h] = mw;
-        l[h] = lw;
-    }
-    if (row == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][h][col * 8 + e] = acc[h][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            s_m[wave][h] = m[h];
-            s_l[wave][h] = l[h];
-        }
-    }
-    __syncthreads();
-
-    // Merge the 4 waves and write either the final fp16 row or the partials.
-    for (int o = threadIdx.x; o < G * D; o += kThreads) {
-        const int h = o / D;
-        const int d = o % D;
-        float mm = s_m[0][h];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) mm = __builtin_fmaxf(mm, s_m[w][h]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = fast_exp2(s_m[w][h] - mm);
-            num = __builtin_fmaf(f, s_acc[w][h][d], num);
-            den = __builtin_fmaf(f, s_l[w][h], den);
-        }
-        if (nparts == 1) {
-            // den is 0 only when no token was read (e.g. every table entry of
-            // the partition was out of range); NaN inputs still propagate.
-            const float r = den == 0.f ? 0.f : num / den;
-            const _Float16 hv = static_cast<_Float16>(r);
-            a.out[out_row0 + o] = __builtin_bit_cast(uint16_t, hv);
-        } else {
-            const size_t prow = (static_cast<size_t>(s) * a.num_q_heads + h0 + h) * a.max_parts + part;
-            a.part_o[prow * D + d] = num;
-            if (d == 0) {
-                a.part_ml[2 * prow] = mm;
-                a.part_ml[2 * prow + 1] = den;
-            }
-        }
-    }
+    const int u = blockIdx.x;
+    const int64_t start = static_cast<int64_t>(u) * U / N;
+    const int64_t end = static_cast<int64_t>(u + 1) * U / N;
+    if (start < end) process_split(u, start, end);
 }
 
-// Merge split-K partials: one wave per (sequence, query head).
-template <int D>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a) {
-    extern __shared__ float s_w[];
-    constexpr int PER_LANE = D / kWave;        // 1 or 2 columns per lane
-    const int lane = threadIdx.x;
-    const int sh = blockIdx.x;                 // s * Hq + h
-    const int s = sh / a.num_q_heads;
-    const int T = a.partition_tokens;
-    int L = a.context_lens[s];
-    L = L < 0 ? 0 : (L > a.max_tokens ? a.max_tokens : L);
-    const int nparts = (L + T - 1) / T;
-    if (nparts <= 1) return;                   // written by the partition kernel
-
-    const float* ml = a.part_ml + static_cast<size_t>(sh) * a.max_parts * 2;
-    float mloc = kNegBig;
-    for (int i = lane; i < nparts; i += kWave) mloc = __builtin_fmaxf(mloc, ml[2 * i]);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) mloc = __builtin_fmaxf(mloc, shfl_xor(mloc, o));
-    float den = 0.f;
-    for (int i = lane; i < nparts; i += kWave) {
-        const float w = fast_exp2(ml[2 * i] - mloc);
-        s_w[i] = w;
-        den = __builtin_fmaf(w, ml[2 * i + 1], den);
+// Merge the partials of pairs that span several splits, and write the zero
+// rows of empty contexts.  One workgroup of 4 waves per (sequence, KV head)
+// pair; pairs the split kernel wrote whole return at once.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int Hkv = a.num_kv_heads;
+    const int N = a.num_splits;
+    const int s = blockIdx.x / Hkv;
+    const int g = blockIdx.x % Hkv;
+    const int L = uniform(clamped_len(a, s));
+    if (L == 0) {
+        for (int o = threadIdx.x; o < G * D; o += kThreads)
+            a.out[(static_cast<size_t>(s) * a.num_q_heads + g * G) * D + o] = 0;
+        return;
     }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) den += shfl_xor(den, o);
-    __syncthreads();
-
-    const float* po = a.part_o + static_cast<size_t>(sh) * a.max_parts * D + lane * PER_LANE;
-    float acc[PER_LANE];
-#pragma unroll
-    for (int e = 0; e < PER_LANE; ++e) acc[e] = 0.f;
-    int i = 0;
-    for (; i + 4 <= nparts; i += 4) {
-        float x[4][PER_LANE];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < PER_LANE; ++e) x[u][e] = po[static_cast<size_t>(i + u) * D + e];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < PER_LANE; ++e) acc[e] = __builtin_fmaf(s_w[i + u], x[u][e], acc[e]);
+    const int nch = chunks_of(L);
+    // Chunks before this pair, and in total.
+    int64_t before = 0, total = 0;
+    for (int b0 = 0; b0 < a.num_seqs; b0 += kWave) {
+        const int sl = b0 + lane;
+        const int64_t n = sl < a.num_seqs ? chunks_of(clamped_len(a, sl)) : 0;
+        total += wave_sum64(n);
+        before += wave_sum64(sl < s ? n : 0);
     }
-    for (; i < nparts; ++i)
+    const int64_t U = uniform64(total) * Hkv;
+    const int64_t first = uniform64(before) * Hkv + static_cast<int64_t>(g) * nch;
+    const int w0 = owner_of(first, U, N);
+    const int w1 = owner_of(first + nch - 1, U, N);
+    if (w0 == w1) return;                      // written whole by the split kernel
+    auto empty_split = [&](int64_t v) { return v * U / N == (v + 1) * U / N; };
+    // Combine the partials of pair (s, g) from splits w0..w1 (skipping empty
+    // ones), in split order, into its fp16 output rows.  The (max, sum) of
+    // each partial are staged in LDS in batches of kBatch splits; each thread
+    // folds them, with its partial outputs, into a running online-softmax
+    // state for the G*D/256 outputs it owns.
+    {
+        constexpr int kOut = (G * D + kThreads - 1) / kThreads;   // outputs per thread
+        constexpr int kBatch = kWaves * D / 2;                    // splits per LDS batch
+        __shared__ float s_pm[kBatch * G];                        // [kBatch][G] max
+        __shared__ float s_pl[kBatch * G];                        // [kBatch][G] sum
+        const size_t pair = static_cast<size_t>(s) * Hkv + g;
+        const bool may_be_empty = U < N;
+        float rm[kOut], rnum[kOut], rden[kOut];
 #pragma unroll
-        for (int e = 0; e < PER_LANE; ++e)
-            acc[e] = __builtin_fmaf(s_w[i], po[static_cast<size_t>(i) * D + e], acc[e]);
-
-    uint16_t* out = a.out + static_cast<size_t>(sh) * D + lane * PER_LANE;
+        for (int j = 0; j < kOut; ++j) {
+            rm[j] = kNegBig;
+            rnum[j] = 0.f;
+            rden[j] = 0.f;
+        }
+        for (int b0 = w0; b0 <= w1; b0 += kBatch) {
+            const int nb = w1 - b0 + 1 < kBatch ? w1 - b0 + 1 : kBatch;
+            __syncthreads();                  // the previous batch is done
+            for (int i = threadIdx.x; i < nb * G; i += kThreads) {
+                const int v = b0 + i / G;
+                const int h = i % G;
+                float pm = -__builtin_inff(), pl = 0.f;
+                if (!may_be_empty || !empty_split(v)) {
+                    const size_t r = (v + pair) * G + h;
+                    pm = a.part_ml[r * 2];
+                    pl = a.part_ml[r * 2 + 1];
+                }
+                s_pm[i] = pm;
+                s_pl[i] = pl;
+            }
+            __syncthreads();
 #pragma unroll
-    for (int e = 0; e < PER_LANE; ++e) {
-        const float r = den == 0.f ? 0.f : acc[e] / den;
-        out[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
+            for (int j = 0; j < kOut; ++j) {
+                const int o = threadIdx.x + j * kThreads;
+                if (o >= G * D) break;
+                const int h = o / D;
+                const int d = o % D;
+                float bm = rm[j];
+                for (int i = 0; i < nb; ++i) bm = __builtin_fmaxf(bm, s_pm[i * G + h]);
+                const float sc = fast_exp2(rm[j] - bm);
+                float num = rnum[j] * sc, den = rden[j] * sc;
+                constexpr int kU = 8;             // partial outputs loaded together
+                for (int i0 = 0; i0 < nb; i0 += kU) {
+                    float po[kU];
+#pragma unroll
+                    for (int t = 0; t < kU; ++t) {
+                        const int i = i0 + t;
+                        po[t] = 0.f;
+                        if (i < nb && s_pm[i * G + h] != -__builtin_inff())
+                            po[t] = a.part_o[((b0 + i + pair) * G + h) * D + d];
+                    }
+#pragma unroll
+                    for (int t = 0; t < kU; ++t) {
+                        const int i = i0 + t;
+                        if (i >= nb) break;
+                        const float f = fast_exp2(s_pm[i * G + h] - bm);
+                        den = __builtin_fmaf(f, s_pl[i * G + h], den);
+                        num = __builtin_fmaf(f, po[t], num);
+                    }
+                }
+                rm[j] = bm;
+                rnum[j] = num;
+                rden[j] = den;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kOut; ++j) {
+            const int o = threadIdx.x + j * kThreads;
+            if (o >= G * D) break;
+            const int h = o / D;
+            const int d = o % D;
+            const float r = rden[j] == 0.f ? 0.f : rnum[j] / rden[j];
+            a.out[(static_cast<size_t>(s) * a.num_q_heads + g * G + h) * D + d] =
+                __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
+        }
     }
 }
 
 template <int D, int BS, int G>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-    const unsigned grid = static_cast<unsigned>(a.num_seqs) * a.max_parts * a.num_kv_heads;
-    hipLaunchKernelGGL((decode_partition_kernel<D, BS, G>), dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_split_kernel<D, BS, G>), dim3(a.num_splits), dim3(kThreads), 0,
                        stream, a);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.max_parts <= 1) return err;
-    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.num_seqs * a.num_q_heads), dim3(kWave),
-                       static_cast<size_t>(a.max_parts) * sizeof(float), stream, a);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.num_seqs * a.num_kv_heads), dim3(kThreads), 0,
+                       stream, a);
     return hipGetLastError();
+}
+
+// Workgroups of decode_split_kernel<D, BS, G> the current device holds at
+// once (occupancy x compute units), cached per device; 0 if unknown.
+template <int D, int BS, int G>
+int resident_one() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, BS, G>,
+                                                     kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    v = per_cu * cus;
+    if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int D, int BS>
+int resident_group(int group) {
+    switch (group) {
+        case 1: return resident_one<D, BS, 1>();
+        case 2: return resident_one<D, BS, 2>();
+        case 4: return resident_one<D, BS, 4>();
+        case 8: return resident_one<D, BS, 8>();
+        default: return 0;
+    }
+}
+
+template <int D>
+int resident_block(int block_size, int group) {
+    switch (block_size) {
+        case 8: return resident_group<D, 8>(group);
+        case 16: return resident_group<D, 16>(group);
+        case 32: return resident_group<D, 32>(group);
+        case 64: return resident_group<D, 64>(group);
+        default: return 0;
+    }
 }
 
 template <int D, int BS>
@@ -498,6 +717,12 @@ bool decode_supported(int head_dim, int block_size, int group) {
     const bool b_ok = block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
     const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
     return d_ok && b_ok && g_ok;
+}
+
+int decode_resident_workgroups(int head_dim, int block_size, int group) {
+    if (head_dim == 128) return resident_block<128>(block_size, group);
+    if (head_dim == 64) return resident_block<64>(block_size, group);
+    return 0;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -16,8 +16,8 @@ struct DecodeArgs {
     const int32_t* block_tables;   // [B][M]
     const int32_t* context_lens;   // [B]
     uint16_t* out;                 // fp16 [B][Hq][D]
-    float* part_o;                 // fp32 [B][Hq][P][D]     (P > 1 only)
-    float* part_ml;                // fp32 [B][Hq][P][2]     (running max, sum)
+    float* part_o;                 // fp32 [N + B*Hkv][G][D]  partial outputs per slot
+    float* part_ml;                // fp32 [N + B*Hkv][G][2]  (running max, sum) per slot
     int32_t num_blocks;
     int32_t block_size;
     int32_t num_kv_heads;
@@ -26,12 +26,14 @@ struct DecodeArgs {
     int32_t num_seqs;
     int32_t max_blocks_per_seq;    // M, row stride of block_tables
     int32_t max_tokens;            // clamp of context lengths
-    int32_t partition_tokens;      // T
-    int32_t max_parts;             // P = ceil(max_context_len / T), >= 1
+    int32_t num_splits;            // N: equal pieces of the chunk list, one workgroup each
     float scale_log2;              // scale * log2(e)
 };
 
 bool decode_supported(int head_dim, int block_size, int group);
+// Workgroups of the decode kernel for these shapes that the current device
+// holds at once; 0 when no device can be queried.
+int decode_resident_workgroups(int head_dim, int block_size, int group);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_store_kvcache(const void* k, const void* v, const int32_t* slots,

@@ -120,7 +120,7 @@ def build(wl, plan_fn=None, fill="sentinel", store_prior=True):
     }
 
 
-def run_step(p, partition_tokens=0):
+def run_step(p, num_splits=0):
     """Library: copy-on-write copies, store, decode (one layer)."""
     wl = p["wl"]
     if p["cows"].numel():
@@ -129,9 +129,9 @@ def run_step(p, partition_tokens=0):
     say(f"{wl.name}: pa_store_kvcache of {p['slots'].numel()} step tokens")
     pa.pa_store_kvcache(p["k_new"], p["v_new"], p["slots"], p["kc"], p["vc"])
     say(f"{wl.name}: pa_decode B={p['q'].shape[0]} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
-        f"D={wl.head_dim} bs={wl.block_size} max_ctx={p['max_ctx']} T={partition_tokens}")
+        f"D={wl.head_dim} bs={wl.block_size} max_ctx={p['max_ctx']} W={num_splits}")
     out = pa.pa_decode(p["q"], p["kc"], p["vc"], p["tables"], p["lens"], wl.scale,
-                       max_context_len=p["max_ctx"], partition_tokens=partition_tokens)
+                       max_context_len=p["max_ctx"], num_splits=num_splits)
     torch.cuda.synchronize()
     return out
 

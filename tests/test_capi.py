@@ -41,12 +41,12 @@ def _desc(nb=64, bs=16, hkv=4, d=64):
 
 def call_decode(desc=None, **kw):
     args = dict(q=0x1000, k=0x2000, v=0x3000, tables=0x4000, M=4, lens=0x5000, B=4, hq=4,
-                max_ctx=33, scale=0.125, out=0x6000, part=0, ws=None, ws_bytes=0)
+                max_ctx=33, scale=0.125, out=0x6000, split=0, ws=None, ws_bytes=0)
     args.update(kw)
     d = desc if desc is not None else _desc()
     return pa.lib().pa_decode(args["q"], args["k"], args["v"], ctypes.byref(d) if d else None,
                               args["tables"], args["M"], args["lens"], args["B"], args["hq"],
-                              args["max_ctx"], args["scale"], args["out"], args["part"],
+                              args["max_ctx"], args["scale"], args["out"], args["split"],
                               args["ws"], args["ws_bytes"], None)
 
 
@@ -63,10 +63,11 @@ NAMES = {v: k for k, v in pa.STATUS.items()}
     (dict(), _desc(d=96), "UNSUPPORTED"),
     (dict(), _desc(bs=4), "UNSUPPORTED"),
     (dict(hq=12), None, "UNSUPPORTED"),            # group 3
-    (dict(part=24), None, "RANGE"),
-    (dict(part=8192), None, "RANGE"),
-    (dict(max_ctx=100000, part=16), None, "WORKSPACE"),
-    (dict(max_ctx=100000, part=16, ws=0x7000, ws_bytes=10), None, "WORKSPACE"),
+    (dict(split=-1), None, "RANGE"),
+    (dict(split=(1 << 20) + 1), None, "RANGE"),
+    (dict(split=16), None, "WORKSPACE"),
+    (dict(split=16, ws=0x7000, ws_bytes=10), None, "WORKSPACE"),
+    (dict(split=16, ws=0x7010, ws_bytes=1 << 20), None, "ALIGN"),
     (dict(), _desc(nb=0), "SHAPE"),
 ])
 def test_decode_rejects_bad_arguments(kw, desc, code):
@@ -102,13 +103,13 @@ def test_copy_blocks_rejects_bad_arguments():
     assert f(0x1000, 0x2000, ctypes.byref(d), None, 0, None) == 0
 
 
-def test_workspace_and_partition_queries():
+def test_workspace_and_split_queries():
     d = _desc(nb=8192, bs=16, hkv=8, d=128)
-    assert pa.pa_decode_partition_tokens(d, 4, 32, 131072, 512) == 512
-    # 4 sequences x 32 heads x 256 partitions x (2 + 128) floats
-    assert pa.pa_decode_workspace_bytes(d, 4, 32, 131072, 512) == 4 * 32 * 256 * 130 * 4
-    t = pa.pa_decode_partition_tokens(d, 32, 32, 2048, 0)
-    assert t % 16 == 0 and 256 <= t <= 4096
-    one = _desc(nb=8192, bs=16, hkv=32, d=128)
-    assert pa.pa_decode_workspace_bytes(one, 32, 32, 2048, 2048) == 0     # one partition
-    assert pa.pa_decode_workspace_bytes(d, 4, 33, 100, 0) == 0             # invalid -> 0
+    assert pa.pa_decode_num_splits(d, 32, 512) == 512
+    # (512 splits + 4 sequences x 8 KV heads) slots x 4 heads x (2 + 128) floats
+    assert pa.pa_decode_workspace_bytes(d, 4, 32, 512) == (512 + 32) * 4 * (2 + 128) * 4
+    n = pa.pa_decode_num_splits(d, 32, 0)
+    assert n > 0
+    assert pa.pa_decode_workspace_bytes(d, 4, 32, 0) == (n + 32) * 4 * (2 + 128) * 4
+    assert pa.pa_decode_workspace_bytes(d, 4, 33, 0) == 0             # invalid -> 0
+    assert pa.pa_decode_num_splits(d, 32, -3) == 0

@@ -49,12 +49,16 @@ def test_decode_small_matches_oracle(name):
     check_close(out, oracle_out(p, kc, vc), name)
 
 
-@pytest.mark.parametrize("T", [16, 48, 256, 512, 4096, 0])
-def test_decode_partition_sizes_match_oracle(T):
+# 1: one split walks every pair; 5, 37: ranges end mid-pair; 1000: more
+# splits than workgroups (the queue hands out the rest); 2000: about one chunk
+# per split; 4000: more splits than chunks (empty ranges between a pair's
+# owners); 0: the device default.
+@pytest.mark.parametrize("N", [1, 5, 37, 256, 1000, 2000, 4000, 0])
+def test_decode_split_sizes_match_oracle(N):
     p = build(MEDIUM, plan_fn=medium_plan())
-    out = run_step(p, partition_tokens=T)
+    out = run_step(p, num_splits=N)
     kc, vc = oracle_caches(p)
-    check_close(out, oracle_out(p, kc, vc), f"T={T}")
+    check_close(out, oracle_out(p, kc, vc), f"N={N}")
 
 
 @pytest.mark.parametrize("bs", [8, 32, 64])
@@ -62,17 +66,17 @@ def test_decode_block_sizes_medium(bs):
     wl = W.shrink(MEDIUM, name=f"medium_bs{bs}", block_size=bs,
                   num_blocks=1024 * 16 // bs, max_blocks_per_seq=4096 // bs)
     p = build(wl, plan_fn=medium_plan(wl))
-    out = run_step(p, partition_tokens=512)
+    out = run_step(p, num_splits=97)
     kc, vc = oracle_caches(p)
     check_close(out, oracle_out(p, kc, vc), f"bs={bs}")
 
 
 def test_decode_is_deterministic_and_placement_invariant():
     p = build(MEDIUM, plan_fn=medium_plan())
-    out1 = run_step(p, partition_tokens=256)
+    out1 = run_step(p, num_splits=300)
     say("decode again")
     out2 = pa.pa_decode(p["q"], p["kc"], p["vc"], p["tables"], p["lens"], MEDIUM.scale,
-                        max_context_len=p["max_ctx"], partition_tokens=256)
+                        max_context_len=p["max_ctx"], num_splits=300)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     nb = MEDIUM.num_blocks
@@ -82,7 +86,7 @@ def test_decode_is_deterministic_and_placement_invariant():
     t2 = torch.where(p["tables"] >= 0, pi[p["tables"].clamp(min=0).long()].int(), p["tables"])
     say("decode on permuted placement")
     out3 = pa.pa_decode(p["q"], k2, v2, t2.contiguous(), p["lens"], MEDIUM.scale,
-                        max_context_len=p["max_ctx"], partition_tokens=256)
+                        max_context_len=p["max_ctx"], num_splits=300)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
 
@@ -97,7 +101,7 @@ def small_prefix_plan(a):
 
 def test_shared_prefix_equals_private_copies_bitwise():
     p = build(SMALL_PREFIX, plan_fn=small_prefix_plan)
-    out_shared = run_step(p, partition_tokens=128)
+    out_shared = run_step(p, num_splits=50)
     kc, vc = oracle_caches(p)
     check_close(out_shared, oracle_out(p, kc, vc), "prefix")
     # private copies of every shared block, made on the device
@@ -127,7 +131,7 @@ def test_shared_prefix_equals_private_copies_bitwise():
     say("decode on private copies")
     out_private = pa.pa_decode(p["q"], k2, v2, torch.from_numpy(t2).to(DEV), p["lens"],
                                SMALL_PREFIX.scale, max_context_len=p["max_ctx"],
-                               partition_tokens=128)
+                               num_splits=50)
     torch.cuda.synchronize()
     assert torch.equal(out_shared.view(torch.int16), out_private.view(torch.int16))
 
@@ -135,7 +139,7 @@ def test_shared_prefix_equals_private_copies_bitwise():
 def test_garbage_in_unused_slots_does_not_leak():
     """NaN-filled vs zero-filled unused slots and table padding: same bits."""
     p = build(MEDIUM, plan_fn=medium_plan())
-    out_nan = run_step(p, partition_tokens=256)
+    out_nan = run_step(p, num_splits=300)
     assert torch.isfinite(out_nan.float()).all()
     mask = np.zeros(MEDIUM.num_blocks * MEDIUM.block_size, dtype=bool)
     from tests.gpu_problems import used_slot_mask
@@ -148,7 +152,7 @@ def test_garbage_in_unused_slots_does_not_leak():
     t0[t0 < 0] = 7          # padding entries now point at a real block
     say("decode with zeroed unused slots")
     out_zero = pa.pa_decode(p["q"], k0, v0, t0, p["lens"], MEDIUM.scale,
-                            max_context_len=p["max_ctx"], partition_tokens=256)
+                            max_context_len=p["max_ctx"], num_splits=300)
     torch.cuda.synchronize()
     assert torch.equal(out_nan.view(torch.int16), out_zero.view(torch.int16))
 
@@ -165,13 +169,13 @@ def test_single_token_context_returns_value_row_exactly():
 
 def test_empty_context_gives_zero_rows():
     p = build(MEDIUM, plan_fn=medium_plan())
-    run_step(p, partition_tokens=256)         # caches now hold the step's tokens
+    run_step(p, num_splits=300)         # caches now hold the step's tokens
     lens = p["lens"].clone()
     lens[2] = 0
     out = torch.full_like(p["q"], float("nan"))
     say("decode with an empty context")
     pa.pa_decode(p["q"], p["kc"], p["vc"], p["tables"], lens, MEDIUM.scale, out=out,
-                 max_context_len=p["max_ctx"], partition_tokens=256)
+                 max_context_len=p["max_ctx"], num_splits=300)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out[2]).item() == 0
     kc, vc = oracle_caches(p)
@@ -185,7 +189,7 @@ def test_empty_context_gives_zero_rows():
 def test_peaky_queries():
     """q = 2 K[p*]: the softmax concentrates on one token; out ~ V[p*]."""
     p = build(MEDIUM, plan_fn=medium_plan())
-    run_step(p, partition_tokens=256)          # caches now hold the step's tokens
+    run_step(p, num_splits=300)          # caches now hold the step's tokens
     kc, vc = oracle_caches(p)
     r = p["ref"]
     rng = np.random.default_rng(17)
@@ -199,7 +203,7 @@ def test_peaky_queries():
     qd = torch.from_numpy(q).to(DEV)
     say("decode with peaky queries")
     out = pa.pa_decode(qd, p["kc"], p["vc"], p["tables"], p["lens"], MEDIUM.scale,
-                       max_context_len=p["max_ctx"], partition_tokens=256)
+                       max_context_len=p["max_ctx"], num_splits=300)
     torch.cuda.synchronize()
     ref = decode_ref(q, kc.view(np.float16), vc.view(np.float16), r["tables"], r["lens"],
                      MEDIUM.scale)
@@ -209,7 +213,7 @@ def test_peaky_queries():
 def test_out_of_range_table_entry_is_skipped_not_read():
     """Without validation a bad entry must not fault: its block counts as empty."""
     p = build(MEDIUM, plan_fn=medium_plan())
-    run_step(p, partition_tokens=256)
+    run_step(p, num_splits=300)
     s = 4                                           # 2049 tokens: last block holds 1 token
     L = int(p["plan"].context_lens[s])
     last = (L - 1) // MEDIUM.block_size
@@ -217,7 +221,7 @@ def test_out_of_range_table_entry_is_skipped_not_read():
     bad[s, last] = MEDIUM.num_blocks + 1000
     say("decode with an out-of-range table entry")
     out = pa.pa_decode(p["q"], p["kc"], p["vc"], bad, p["lens"], MEDIUM.scale,
-                       max_context_len=p["max_ctx"], partition_tokens=256)
+                       max_context_len=p["max_ctx"], num_splits=300)
     torch.cuda.synchronize()
     kc, vc = oracle_caches(p)
     r = p["ref"]
@@ -230,11 +234,11 @@ def test_out_of_range_table_entry_is_skipped_not_read():
     try:
         with pytest.raises(pa.PaError) as e:
             pa.pa_decode(p["q"], p["kc"], p["vc"], bad, p["lens"], MEDIUM.scale,
-                         max_context_len=p["max_ctx"], partition_tokens=256)
+                         max_context_len=p["max_ctx"], num_splits=300)
         assert e.value.code == "RANGE"
         with pytest.raises(pa.PaError) as e:
             pa.pa_decode(p["q"], p["kc"], p["vc"], p["tables"], p["lens"], MEDIUM.scale,
-                         max_context_len=100, partition_tokens=256)
+                         max_context_len=100, num_splits=300)
         assert e.value.code == "RANGE"
     finally:
         pa.pa_set_validate(prev)
@@ -248,8 +252,7 @@ FULL = [("mha", [0, 13, 31]), ("mix", None), ("prefix", [0, 31, 62, 63]),
 def test_decode_full_size_sampled(name, seqs):
     wl = W.ALL.get(name) or W.long_workload(int(name.split("bs")[1]))
     p = build(wl, fill="random")
-    T = 512 if name.startswith("long") else 0
-    out = run_step(p, partition_tokens=T)
+    out = run_step(p)
     if seqs is None:     # mix: the shortest, the longest and two in between
         order = np.argsort(p["ref"]["lens"])
         seqs = [int(order[0]), int(order[10]), int(order[20]), int(order[-1])]
