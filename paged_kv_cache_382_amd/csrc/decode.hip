@@ -192,7 +192,16 @@ void decode_split_kernel(const DecodeArgs a) {
     // Per-lane byte offset inside a load: row `row` of the load, 16-byte column `col`.
     const uint32_t lane_off = row * row_bytes + col * 16;
 
-    const int64_t U = chunks_per_head(a, lane) * Hkv;
+    // With at most 64 sequences, one load of the context lengths (lane i holds
+    // sequence i) serves the total, the search for the first pair and the walk
+    // from pair to pair; larger batches read them again as needed.
+    const bool lens_in_regs = a.num_seqs <= kWave;
+    const int len_reg = (lens_in_regs && lane < a.num_seqs) ? clamped_len(a, lane) : 0;
+    const int64_t incl_reg = wave_incl_scan64(chunks_of(len_reg), lane);
+    const int64_t U = (lens_in_regs ? readlane64(incl_reg, kWave - 1) : chunks_per_head(a, lane)) * Hkv;
+    auto len_of = [&](int sq) {
+        return lens_in_regs ? __builtin_amdgcn_readlane(len_reg, sq) : clamped_len(a, sq);
+    };
 
     // Process the chunks [start, end) of split `unit`: walk the pairs they
     // cover; each piece of a pair (a segment) is reduced by the workgroup and
@@ -202,7 +211,16 @@ void decode_split_kernel(const DecodeArgs a) {
         // chunk total (times Hkv) passes it.
         int s = 0, L = 0, nch = 0;
         int64_t seq_base = 0;        // Hkv * chunks of all earlier sequences
-        {
+        if (lens_in_regs) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.num_seqs && incl_reg * Hkv > start);
+            if (hit) {
+                const int f = __builtin_ctzll(hit);
+                s = f;
+                L = __builtin_amdgcn_readlane(len_reg, f);
+                nch = chunks_of(L);
+                seq_base = (readlane64(incl_reg, f) - nch) * Hkv;
+            }
+        } else {
             int64_t base = 0;
             for (int b0 = 0; b0 < a.num_seqs; b0 += kWave) {
                 const int sl = b0 + lane;
@@ -507,7 +525,7 @@ void decode_split_kernel(const DecodeArgs a) {
             if (++g == Hkv) {
                 g = 0;
                 L = 0;
-                while (L == 0 && s + 1 < a.num_seqs) L = clamped_len(a, ++s);
+                while (L == 0 && s + 1 < a.num_seqs) L = len_of(++s);
                 nch = chunks_of(L);
                 if (nch == 0) break;     // not reached while pos < end
             }
@@ -570,6 +588,23 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
             rnum[j] = 0.f;
             rden[j] = 0.f;
         }
+        // The first kU partial outputs of each owned output are loaded before
+        // the (max, sum) staging so that both round trips overlap.
+        constexpr int kU = 8;
+        float po0[kOut][kU];
+#pragma unroll
+        for (int j = 0; j < kOut; ++j) {
+            const int o = threadIdx.x + j * kThreads;
+            const int h = o / D;
+            const int d = o % D;
+#pragma unroll
+            for (int t = 0; t < kU; ++t) {
+                const int v = w0 + t;
+                po0[j][t] = 0.f;
+                if (o < G * D && v <= w1 && (!may_be_empty || !empty_split(v)))
+                    po0[j][t] = a.part_o[((v + pair) * G + h) * D + d];
+            }
+        }
         for (int b0 = w0; b0 <= w1; b0 += kBatch) {
             const int nb = w1 - b0 + 1 < kBatch ? w1 - b0 + 1 : kBatch;
             __syncthreads();                  // the previous batch is done
@@ -596,12 +631,15 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
                 for (int i = 0; i < nb; ++i) bm = __builtin_fmaxf(bm, s_pm[i * G + h]);
                 const float sc = fast_exp2(rm[j] - bm);
                 float num = rnum[j] * sc, den = rden[j] * sc;
-                constexpr int kU = 8;             // partial outputs loaded together
                 for (int i0 = 0; i0 < nb; i0 += kU) {
                     float po[kU];
 #pragma unroll
                     for (int t = 0; t < kU; ++t) {
                         const int i = i0 + t;
+                        if (b0 == w0 && i0 == 0) {
+                            po[t] = po0[j][t];
+                            continue;
+                        }
                         po[t] = 0.f;
                         if (i < nb && s_pm[i * G + h] != -__builtin_inff())
                             po[t] = a.part_o[((b0 + i + pair) * G + h) * D + d];
