@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured as one HIP graph (reported under 'graph')")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over half the pool of one layer (a plain copy "
                          "of known size, for scaling the HBM byte counters) and exit")
@@ -257,7 +259,7 @@ def main():
     cows = torch.tensor([list(c) for c in plan.cow_pairs], dtype=torch.int32,
                         device=dev).reshape(-1, 2)
     desc = pa.CacheDesc(*shape)
-    splits = pa.pa_decode_num_splits(desc, hq, args.splits)
+    splits = args.splits                 # 0: the library's choice for this batch
     ws = pa.decode_workspace(desc, B, hq, splits, dev)
 
     def step(events=None):
@@ -289,6 +291,21 @@ def main():
     dec_ms = [e[0].elapsed_time(e[1]) for row in events for e in row]
     dec_avg_ms = float(np.mean(dec_ms))
 
+    graph = None
+    if args.graph:
+        g = pa.DecodeStepGraph(caches, q, k_new, v_new, slots, tables, lens_d, wl.scale, out,
+                               cow_pairs=cows, max_context_len=max_ctx, num_splits=splits)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(args.steps):
+            g.replay()
+        ge.record()
+        torch.cuda.synchronize()
+        graph = gs.elapsed_time(ge) / args.steps
+
     n_dec = decode_bytes(lens, hq, hkv, d, bs)
     n_step = layers * (n_dec + store_bytes(B, hkv, d) + copy_bytes(len(plan.cow_pairs), bs, hkv, d))
     value = n_step / (step_ms * 1e-3) / 1e9
@@ -311,7 +328,7 @@ def main():
             "workload": describe(wl, plan),
             "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
             "context_min": min(lens), "context_max": max_ctx, "context_sum": sum(lens),
-            "layers": layers, "num_splits": splits, "pool_blocks": wl.num_blocks,
+            "layers": layers, "num_splits": splits or "auto", "pool_blocks": wl.num_blocks,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
@@ -334,6 +351,10 @@ def main():
                       "cow_pairs_this_step": len(plan.cow_pairs)},
         "host_step_us": host_step_cost(wl),
     }
+    if graph is not None:
+        result["graph"] = {"ms_per_step": round(graph, 4),
+                           "value": round(n_step / (graph * 1e-3) / 1e9, 2),
+                           "decode_tokens_per_s": round(B / (graph * 1e-3), 2)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, plan, caches[0][0], caches[0][1], q[0],
                                               args.cpu_budget)

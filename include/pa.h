@@ -151,7 +151,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  *   out            device fp16 [num_seqs][num_q_heads][head_dim] (written)
  *   num_splits     number of equal pieces N the work is cut into, one
  *                  workgroup each; 0 picks as many as the current device
- *                  holds at once.  The 16-token chunks of all (sequence, KV
+ *                  holds at once, but no more than the chunk count can reach
+ *                  (num_seqs * num_kv_heads * ceil(max_context_len / 16)).  The 16-token chunks of all (sequence, KV
  *                  head) pairs, in sequence-major order, are divided into N
  *                  contiguous ranges.  A pair that straddles ranges gets
  *                  fp32 partials (running max, sum, weighted values) from
@@ -185,9 +186,10 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t num_splits);
 
-/* The number of splits N pa_decode uses (resolves 0 from the current
+/* The number of splits pa_decode uses at most (resolves 0 from the current
  * device's occupancy, assuming 1024 resident workgroups when no device can be
- * queried).  Returns 0 for invalid shapes. */
+ * queried; pa_decode may use fewer for a small batch).  Returns 0 for invalid
+ * shapes. */
 int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads,
                              int32_t num_splits);
 

@@ -19,7 +19,7 @@ __all__ = [
     "PaError", "CacheDesc", "lib",
     "pa_store_kvcache", "pa_copy_blocks", "pa_decode",
     "pa_decode_workspace_bytes", "pa_decode_num_splits",
-    "pa_set_validate", "pa_version", "Allocator",
+    "pa_set_validate", "pa_version", "Allocator", "decode_workspace", "DecodeStepGraph",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
@@ -233,6 +233,60 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         float(scale), _dev(out, torch.float16, "out"), int(num_splits), ws_ptr, ws_bytes,
         _stream(stream)))
     return out
+
+
+class DecodeStepGraph:
+    """One decode step of every layer, captured once into a HIP graph.
+
+    A step is, per layer: the copy-on-write block copies (if any), the store of
+    the step's new K/V rows through ``slot_mapping``, and ``pa_decode``.  The
+    launches are recorded once; ``replay()`` then issues the whole step with a
+    single graph launch, without per-kernel launch cost.  As with any graph,
+    the tensors are fixed: update their contents in place between replays
+    (new rows, slots, tables, lengths, queries); shapes and the number of
+    copy pairs cannot change.
+
+    layers: list of (k_cache, v_cache); q, k_new, v_new, out: per-layer lists
+    of tensors (q/out [B, Hq, D], k_new/v_new [N, Hkv, D]); the metadata is
+    shared by all layers.
+    """
+
+    def __init__(self, layers, q, k_new, v_new, slot_mapping, block_tables, context_lens, scale,
+                 out, cow_pairs=None, max_context_len=None, num_splits=0):
+        import torch
+        self.layers = list(layers)
+        self.args = (q, k_new, v_new, slot_mapping, block_tables, context_lens, out, cow_pairs)
+        self.scale = float(scale)
+        self.max_context_len = max_context_len
+        kc0 = self.layers[0][0]
+        desc = cache_desc(kc0)
+        B, hq = q[0].shape[0], q[0].shape[1]
+        self.num_splits = int(num_splits)
+        self.workspace = decode_workspace(desc, B, hq, self.num_splits, kc0.device)
+        # Kernels are loaded (and the pool primed) by one eager step on a side
+        # stream before capture.
+        side = torch.cuda.Stream(device=kc0.device)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self._step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize(kc0.device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._step()
+
+    def _step(self):
+        q, k_new, v_new, slots, tables, lens, out, cows = self.args
+        for layer, (kc, vc) in enumerate(self.layers):
+            if cows is not None and cows.numel():
+                pa_copy_blocks(kc, vc, cows)
+            pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc)
+            pa_decode(q[layer], kc, vc, tables, lens, self.scale, out=out[layer],
+                      max_context_len=self.max_context_len, num_splits=self.num_splits,
+                      workspace=self.workspace)
+
+    def replay(self):
+        self.graph.replay()
 
 
 # --------------------------------------------------------------------------

@@ -223,7 +223,15 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
         return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
     if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
         return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
-    const int32_t splits = pa::resolve_splits(cache, num_q_heads, num_splits);
+    const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
+                                                   max_context_len);
+    int32_t splits = pa::resolve_splits(cache, num_q_heads, num_splits);
+    if (num_splits == 0) {
+        // No more splits than chunks can exist: small batches launch a small grid.
+        const int64_t chunk_bound = static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
+                                    ((max_tokens64 + 15) / 16);
+        splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, chunk_bound)));
+    }
     const size_t need = pa::workspace_for(cache, num_seqs, num_q_heads, splits);
     if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
     if (workspace_bytes < need)
@@ -232,8 +240,6 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
         return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
     const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
     if (pairs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld pairs)", fn, (long long)pairs);
-    const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
-                                                   max_context_len);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (pa::validate_flag()) {
         std::vector<int32_t> lens, tables;
