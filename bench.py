@@ -196,6 +196,51 @@ def copy_probe(wl, dev, reps):
                       "gbps_read_plus_write": round(n / (ms * 1e-3) / 1e9, 2)}), flush=True)
 
 
+def compaction_probe(wl, dev, reps):
+    """Defragment a scattered pool and time the copies that compaction needs.
+
+    The pool of ``wl`` is scattered by the seeded add/append/free trace, then
+    every other surviving sequence is freed; the C++ allocator plans the
+    compaction (timed on the host) and one many-pair ``pa_copy_blocks`` call
+    moves the blocks of one layer's caches (timed with HIP events, ``reps``
+    launches).  Each launch reads and writes ``copy_bytes(pairs, ...) / 2``
+    bytes.
+    """
+    import torch
+
+    import paged_kv_cache_382_amd as pa
+    alloc = pa.Allocator(wl.num_blocks, wl.block_size, wl.max_blocks_per_seq,
+                         W.free_order(wl.num_blocks, wl.seed))
+    live = W.fragment_pool(alloc, wl.seed + 200, n_ops=10000,
+                           max_tokens=min(8192, wl.max_blocks_per_seq * wl.block_size))
+    for seq in live[::2]:
+        alloc.free_seq(seq)
+    used = alloc.stats()["used_blocks"]
+    t0 = time.perf_counter()
+    pairs = alloc.compact()
+    host_ms = (time.perf_counter() - t0) * 1e3
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    kc = torch.zeros(shape, dtype=torch.float16, device=dev)
+    vc = torch.zeros_like(kc)
+    pairs_dev = torch.from_numpy(np.ascontiguousarray(pairs)).to(dev)
+    n = copy_bytes(len(pairs), wl.block_size, wl.num_kv_heads, wl.head_dim)
+    pa.pa_copy_blocks(kc, vc, pairs_dev)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        pa.pa_copy_blocks(kc, vc, pairs_dev)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    gbps = n / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "compaction": wl.name, "used_blocks": used, "pairs": len(pairs),
+        "host_plan_ms": round(host_ms, 3), "bytes_per_launch": n, "launches": reps + 1,
+        "us_per_launch": round(ms * 1e3, 3), "gbps_read_plus_write": round(gbps, 2),
+        "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,10 +257,13 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over half the pool of one layer (a plain copy "
                          "of known size, for scaling the HBM byte counters) and exit")
+    ap.add_argument("--compaction", action="store_true",
+                    help="only plan a compaction of the scattered pool and time its block "
+                         "copies for one layer, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only; --gpus must be 1 (multi-GPU runs are not "
-              "part of this build)", file=sys.stderr)
+        print("bench.py measures one GPU only; --gpus must be 1 (the library has no "
+              "multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -228,6 +276,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe:
         copy_probe(wl, dev, max(args.steps, 1))
+        return
+    if args.compaction:
+        compaction_probe(wl, dev, max(args.steps, 1))
         return
 
     alloc = pa.Allocator(wl.num_blocks, wl.block_size, wl.max_blocks_per_seq,

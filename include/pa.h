@@ -282,6 +282,56 @@ int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap);
 pa_status pa_alloc_seq_info(const pa_allocator* a, int64_t seq,
                             int32_t* n_tokens, int32_t* n_blocks);
 
+/* Register sequence `seq` by its token ids, sharing cached full blocks.
+ *
+ * Source: [PA-mem] "Architectural limits" and "Engineering: configuration
+ * and monitoring" (prefix caching; its hit rate as a metric); [vLLM-core]
+ * section 2 (pages of a common prefix are shared).
+ *
+ * tokens: host int32 [n_tokens].  Every full block is keyed by a chained
+ * content hash: 64-bit FNV-1a over the previous block's key (8 bytes,
+ * little-endian; 0 for the first block) and the block's token ids (4 bytes
+ * each, little-endian).  The leading run of full blocks whose key, token ids
+ * and previous block all match a live cached block is shared (reference
+ * count + 1); the rest are taken from the free list, and each new full block
+ * whose key is not yet cached is cached.  A partial last block is never
+ * cached or shared; blocks filled later by appends are not cached.  A block
+ * leaves the cache when its reference count reaches 0.
+ *
+ * slots_out (nullable, host int32 [n_tokens]) receives every token's slot;
+ * *n_cached receives the number of leading tokens whose K/V already sit in
+ * shared blocks (a multiple of block_size): the caller stores only tokens
+ * from *n_cached on.  Errors as pa_alloc_add_seq, with the shared blocks not
+ * counted against the free list. */
+pa_status pa_alloc_add_seq_tokens(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                  int32_t n_tokens, int32_t* slots_out, int32_t* n_cached);
+
+/* Renumber blocks so that every used block lies below the number of used
+ * blocks u.
+ *
+ * Source: [PA-mem] "Continuous batching and memory management working
+ * together" (compaction against fragmentation, weighed against the cost of
+ * moving data).
+ *
+ * Each used block numbered u or above, in increasing order, takes the lowest
+ * free block below u not yet taken; block tables, reference counts and the
+ * prefix cache follow; the free list becomes u, u+1, ..., num_blocks-1.
+ * pairs_out (host int32 [max_pairs][2]) receives the (src, dst) moves in
+ * increasing src order; every src >= u > every dst, so no move overwrites
+ * another's source and one pa_copy_blocks call on each layer's caches
+ * applies them all.  The caller must make those copies before the next
+ * store or decode that uses the new tables.
+ * *n_pairs always receives the number of moves; if it exceeds max_pairs the
+ * call fails with PA_ERR_RANGE and changes nothing (at most
+ * min(u, num_blocks - u) moves are ever needed). */
+pa_status pa_alloc_compact(pa_allocator* a, int32_t* pairs_out, int32_t max_pairs,
+                           int32_t* n_pairs);
+
+/* Prefix-cache counters: tokens asked for through pa_alloc_add_seq_tokens,
+ * tokens found cached, and blocks currently cached. */
+pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* queried_tokens,
+                                int64_t* hit_tokens, int32_t* cached_blocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ store          raw-bit scatter through ``slot_mapping`` and whole-block copies.
 attention      gather through block tables + dense softmax attention (fp64).
 splitk         the same attention computed over token chunks and recombined.
 bruteforce     a second, scalar-loop coding of ``attention`` for tiny inputs.
-allocator_model  free list, reference counts, fork and copy-on-write.
+allocator_model  free list, reference counts, fork and copy-on-write,
+               content-hash prefix caching and compaction.
 
 Pin status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle.py`` or ``tests/test_allocator_model.py``.
@@ -31,7 +32,7 @@ from .store import store_ref, copy_blocks_ref
 from .attention import gather_sequence, decode_ref
 from .splitk import decode_splitk_ref
 from .bruteforce import decode_bruteforce, store_bruteforce
-from .allocator_model import AllocatorModel, AllocError
+from .allocator_model import AllocatorModel, AllocError, block_hash, fnv1a64
 
 __all__ = [
     "store_ref",
@@ -43,4 +44,6 @@ __all__ = [
     "store_bruteforce",
     "AllocatorModel",
     "AllocError",
+    "block_hash",
+    "fnv1a64",
 ]

@@ -34,6 +34,30 @@ Readings where the pages are silent:
 
 from collections import deque
 
+FNV_OFFSET = 0xCBF29CE484222325
+FNV_PRIME = 0x100000001B3
+MASK64 = (1 << 64) - 1
+
+
+def fnv1a64(data):
+    """64-bit FNV-1a (Fowler, Noll, Vo): start from the offset basis; for each
+    byte, xor it in, then multiply by the FNV prime modulo 2**64."""
+    h = FNV_OFFSET
+    for byte in data:
+        h ^= byte
+        h = (h * FNV_PRIME) & MASK64
+    return h
+
+
+def block_hash(parent_hash, tokens):
+    """Content hash of one full block: FNV-1a over the parent block's hash
+    (8 bytes, little-endian) followed by the block's token ids (4 bytes each,
+    little-endian, two's complement).  The first block of a sequence has
+    parent hash 0."""
+    data = int(parent_hash & MASK64).to_bytes(8, "little")
+    data += b"".join(int(t & 0xFFFFFFFF).to_bytes(4, "little") for t in tokens)
+    return fnv1a64(data)
+
 
 class AllocError(Exception):
     """Raised by a failed operation; ``code`` names the failure."""
@@ -61,6 +85,12 @@ class AllocatorModel:
         self.refcounts = [0] * num_blocks
         self.seqs = {}  # seq id -> [list of physical blocks, number of tokens]
         self.cow_copies = 0
+        # Prefix cache: content hash -> block, and per registered block its
+        # (hash, parent block or -1, token ids).
+        self.index = {}
+        self.block_key = {}
+        self.prefix_queried = 0
+        self.prefix_hits = 0
 
     # -- helpers -----------------------------------------------------------
     def _slot(self, blocks, pos):
@@ -130,13 +160,107 @@ class AllocatorModel:
         return self._slot(blocks, pos), cow[0], cow[1]
 
     def free_seq(self, seq):
-        """Drop a finished sequence; blocks whose count reaches 0 become free."""
+        """Drop a finished sequence; blocks whose count reaches 0 become free
+        (and leave the prefix cache)."""
         blocks, _ = self._get(seq)
         for b in blocks:
             self.refcounts[b] -= 1
             if self.refcounts[b] == 0:
                 self.free.append(b)
+                key = self.block_key.pop(b, None)
+                if key is not None and self.index.get(key[0]) == b:
+                    del self.index[key[0]]
         del self.seqs[seq]
+
+    def add_seq_tokens(self, seq, tokens):
+        """Register a sequence by its token ids, reusing cached full blocks.
+
+        Automatic prefix sharing ([vLLM-core] section 2, pages of a common
+        prefix are shared; [PA-mem] "Architectural limits" and [nano-KV]
+        "Engineering: configuration and monitoring", prefix caching and its hit
+        rate).  Reading: each full block is keyed by the hash chain of
+        ``block_hash``; a leading run of full blocks whose hash, tokens and
+        parent block match a live registered block is shared (reference count
+        + 1) instead of allocated; the first miss ends the run.  Every newly
+        allocated full block is registered; a partial last block never is.
+        Only live blocks are found: a block leaves the cache when it is freed.
+
+        Returns ``(slots, n_cached)``: the slot of every token and how many
+        leading tokens already hold their K/V (whole shared blocks).
+        """
+        if seq in self.seqs:
+            raise AllocError("SEQ_EXISTS", str(seq))
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        bs = self.block_size
+        need_total = -(-n // bs)
+        if need_total > self.max_blocks_per_seq:
+            raise AllocError("SEQ_LIMIT", f"{need_total} blocks")
+        hits, hashes, parent, h = [], [], -1, 0
+        for j in range(n // bs):
+            toks = tuple(tokens[j * bs:(j + 1) * bs])
+            h = block_hash(h, toks)
+            hashes.append(h)
+            if len(hits) == j:
+                b = self.index.get(h)
+                if b is not None and self.block_key[b][1] == parent and self.block_key[b][2] == toks:
+                    hits.append(b)
+                    parent = b
+        need_new = need_total - len(hits)
+        if need_new > len(self.free):
+            raise AllocError("OUT_OF_BLOCKS", f"need {need_new}, have {len(self.free)}")
+        blocks = list(hits)
+        for b in hits:
+            self.refcounts[b] += 1
+        parent = hits[-1] if hits else -1
+        for j in range(len(hits), need_total):
+            b = self.free.popleft()
+            self.refcounts[b] = 1
+            blocks.append(b)
+            if j < n // bs:
+                h = hashes[j]
+                if h not in self.index:
+                    self.index[h] = b
+                    self.block_key[b] = (h, parent, tuple(tokens[j * bs:(j + 1) * bs]))
+                parent = b
+        self.seqs[seq] = [blocks, n]
+        self.prefix_queried += n
+        self.prefix_hits += len(hits) * bs
+        return [self._slot(blocks, p) for p in range(n)], len(hits) * bs
+
+    def compact(self):
+        """Move every used block below the count of used blocks.
+
+        Defragmentation by block remapping ([PA-mem] "Continuous batching and
+        memory management working together": memory compaction, weighed against
+        its migration cost).  Reading: with ``u`` blocks in use, each used block
+        numbered ``u`` or above moves, in increasing order, to the lowest free
+        block below ``u`` not yet taken; every table, reference count and
+        prefix-cache entry follows; the free list becomes ``u .. NB-1`` in
+        increasing order.  Returns the ``(src, dst)`` copies (increasing src)
+        the caller must apply to every cache before using the new tables.
+        """
+        used = sum(1 for r in self.refcounts if r > 0)
+        holes = [b for b in range(used) if self.refcounts[b] == 0]
+        movers = [b for b in range(used, self.num_blocks) if self.refcounts[b] > 0]
+        remap = dict(zip(movers, holes))
+        for entry in self.seqs.values():
+            entry[0] = [remap.get(b, b) for b in entry[0]]
+        for src, dst in remap.items():
+            self.refcounts[dst] = self.refcounts[src]
+            self.refcounts[src] = 0
+        keys = {}
+        for b, (h, parent, toks) in self.block_key.items():
+            keys[remap.get(b, b)] = (h, remap.get(parent, parent), toks)
+        self.block_key = keys
+        self.index = {h: remap.get(b, b) for h, b in self.index.items()}
+        self.free = deque(range(used, self.num_blocks))
+        return sorted(remap.items())
+
+    def prefix_stats(self):
+        """(tokens asked for through add_seq_tokens, tokens found cached,
+        blocks currently in the prefix cache)."""
+        return self.prefix_queried, self.prefix_hits, len(self.index)
 
     def export(self, seq_ids, row_stride):
         """Block tables ``[n][row_stride]`` (padding -1) and context lengths."""

@@ -83,6 +83,9 @@ SIGNATURES = {
     "pa_alloc_num_free": (_I32, [_P]),
     "pa_alloc_free_list": (_I32, [_P, _PI32, _I32]),
     "pa_alloc_seq_info": (ctypes.c_int, [_P, _I64, _PI32, _PI32]),
+    "pa_alloc_add_seq_tokens": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32, _PI32]),
+    "pa_alloc_compact": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
+    "pa_alloc_prefix_stats": (ctypes.c_int, [_P, _PI64, _PI64, _PI32]),
 }
 
 _lib = None
@@ -380,3 +383,29 @@ class Allocator:
 
     def seq_len(self, seq):
         return self.seq_info(seq)[0]
+
+    def add_seq_tokens(self, seq, tokens):
+        """Register a sequence by token ids, sharing cached full blocks;
+        returns (slots, n_cached)."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        n = toks.size
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        n_cached = ctypes.c_int32()
+        _check(lib().pa_alloc_add_seq_tokens(self._h, int(seq), _i32p(toks) if n else None, n,
+                                             _i32p(slots), ctypes.byref(n_cached)))
+        return slots[:n], n_cached.value
+
+    def compact(self):
+        """Renumber used blocks below the used count; returns the [k, 2]
+        (src, dst) copies to apply to every cache."""
+        cap = max(self.num_blocks // 2, 1)
+        pairs = np.empty((cap, 2), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_alloc_compact(self._h, _i32p(pairs), cap, ctypes.byref(n)))
+        return pairs[:n.value]
+
+    def prefix_stats(self):
+        """(tokens queried, tokens found cached, blocks cached)."""
+        q, h, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(lib().pa_alloc_prefix_stats(self._h, ctypes.byref(q), ctypes.byref(h), ctypes.byref(c)))
+        return q.value, h.value, c.value

@@ -14,6 +14,16 @@
 //    common prefix are shared; a shared page is copied only when a sharer
 //    modifies it; reference counts keep a shared page alive until its last
 //    user is done.
+//  * same pages (nano-vLLM, sections "Architectural limits" and
+//    "Engineering: configuration and monitoring"; vLLM core, section 2):
+//    prefix caching -- full blocks of an already cached prompt prefix are
+//    shared rather than recomputed -- and its hit rate as a metric.  Blocks are
+//    keyed by a chained FNV-1a content hash; a hit also compares the tokens
+//    and the parent block, so a hash collision can only cost a miss.
+//  * nano-vLLM page, section "Continuous batching and memory management
+//    working together": memory compaction against fragmentation, at the cost
+//    of moving data.  Compaction here renumbers blocks only; the caller moves
+//    the bytes with the returned copy list.
 //
 // Every operation checks everything it needs before mutating anything, so a
 // failed call leaves the state unchanged.
@@ -32,6 +42,32 @@ struct Seq {
     std::vector<int32_t> blocks;
     int32_t n_tokens = 0;
 };
+
+// What a block was registered with in the prefix cache.
+struct CachedKey {
+    uint64_t hash;
+    int32_t parent;                 // previous block of the chain, -1 for the first
+    std::vector<int32_t> tokens;
+};
+
+constexpr uint64_t kFnvOffset = 0xCBF29CE484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001B3ull;
+
+inline uint64_t fnv_bytes(uint64_t h, uint64_t v, int nbytes) {
+    for (int i = 0; i < nbytes; ++i) {
+        h ^= (v >> (8 * i)) & 0xFF;
+        h *= kFnvPrime;
+    }
+    return h;
+}
+
+// FNV-1a over the parent hash (8 bytes, little-endian) and the token ids
+// (4 bytes each, little-endian).
+uint64_t chain_hash(uint64_t parent_hash, const int32_t* tokens, int32_t n) {
+    uint64_t h = fnv_bytes(kFnvOffset, parent_hash, 8);
+    for (int32_t i = 0; i < n; ++i) h = fnv_bytes(h, static_cast<uint32_t>(tokens[i]), 4);
+    return h;
+}
 
 // Fixed-capacity ring buffer holding the free list.
 class FreeList {
@@ -68,6 +104,10 @@ struct pa_allocator {
     std::vector<int32_t> refcount;
     std::unordered_map<int64_t, Seq> seqs;
     int64_t cow_copies = 0;
+    std::unordered_map<uint64_t, int32_t> prefix_index;    // hash -> live block
+    std::unordered_map<int32_t, CachedKey> cached;          // block -> its key
+    int64_t prefix_queried = 0;
+    int64_t prefix_hits = 0;
 
     pa_allocator(int32_t nb, int32_t bs, int32_t mb)
         : num_blocks(nb), block_size(bs), max_blocks_per_seq(mb), free_list(nb),
@@ -213,8 +253,130 @@ pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq) {
     auto it = a->seqs.find(seq);
     if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_free_seq: unknown sequence %lld", (long long)seq);
     for (int32_t b : it->second.blocks)
-        if (--a->refcount[b] == 0) a->free_list.push_back(b);
+        if (--a->refcount[b] == 0) {
+            a->free_list.push_back(b);
+            auto c = a->cached.find(b);
+            if (c != a->cached.end()) {
+                auto ix = a->prefix_index.find(c->second.hash);
+                if (ix != a->prefix_index.end() && ix->second == b) a->prefix_index.erase(ix);
+                a->cached.erase(c);
+            }
+        }
     a->seqs.erase(it);
+    return ok();
+}
+
+pa_status pa_alloc_add_seq_tokens(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                  int32_t n_tokens, int32_t* slots_out, int32_t* n_cached) {
+    if (!a || !n_cached || (n_tokens > 0 && !tokens))
+        return fail(PA_ERR_NULL, "pa_alloc_add_seq_tokens: NULL argument");
+    if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq_tokens: sequence %lld exists", (long long)seq);
+    if (n_tokens < 0) return fail(PA_ERR_RANGE, "pa_alloc_add_seq_tokens: negative token count");
+    const int32_t bs = a->block_size;
+    const int32_t need = (n_tokens + bs - 1) / bs, full = n_tokens / bs;
+    if (need > a->max_blocks_per_seq)
+        return fail(PA_ERR_SEQ_LIMIT, "pa_alloc_add_seq_tokens: %d blocks exceed the per-sequence limit %d", need, a->max_blocks_per_seq);
+    // Hash every full block; the leading run of matching live blocks is shared.
+    std::vector<uint64_t> hashes(static_cast<size_t>(full));
+    std::vector<int32_t> hits;
+    uint64_t h = 0;
+    int32_t parent = -1;
+    for (int32_t j = 0; j < full; ++j) {
+        const int32_t* tk = tokens + static_cast<size_t>(j) * bs;
+        h = chain_hash(h, tk, bs);
+        hashes[j] = h;
+        if (static_cast<int32_t>(hits.size()) != j) continue;
+        auto ix = a->prefix_index.find(h);
+        if (ix == a->prefix_index.end()) continue;
+        const CachedKey& key = a->cached.at(ix->second);
+        if (key.parent != parent || !std::equal(key.tokens.begin(), key.tokens.end(), tk)) continue;
+        hits.push_back(ix->second);
+        parent = ix->second;
+    }
+    const int32_t n_hit = static_cast<int32_t>(hits.size());
+    if (need - n_hit > a->free_list.size())
+        return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_add_seq_tokens: need %d blocks, %d free", need - n_hit, a->free_list.size());
+    Seq s;
+    s.blocks = hits;
+    for (int32_t b : hits) ++a->refcount[b];
+    parent = n_hit ? hits.back() : -1;
+    for (int32_t j = n_hit; j < need; ++j) {
+        int32_t b = a->free_list.pop_front();
+        a->refcount[b] = 1;
+        s.blocks.push_back(b);
+        if (j < full) {
+            if (!a->prefix_index.count(hashes[j])) {
+                const int32_t* tk = tokens + static_cast<size_t>(j) * bs;
+                a->prefix_index.emplace(hashes[j], b);
+                a->cached[b] = CachedKey{hashes[j], parent, std::vector<int32_t>(tk, tk + bs)};
+            }
+            parent = b;
+        }
+    }
+    s.n_tokens = n_tokens;
+    if (slots_out)
+        for (int32_t p = 0; p < n_tokens; ++p) slots_out[p] = a->slot_of(s, p);
+    a->seqs.emplace(seq, std::move(s));
+    a->prefix_queried += n_tokens;
+    a->prefix_hits += static_cast<int64_t>(n_hit) * bs;
+    *n_cached = n_hit * bs;
+    return ok();
+}
+
+pa_status pa_alloc_compact(pa_allocator* a, int32_t* pairs_out, int32_t max_pairs, int32_t* n_pairs) {
+    if (!a || !n_pairs) return fail(PA_ERR_NULL, "pa_alloc_compact: NULL argument");
+    const int32_t nb = a->num_blocks;
+    int32_t used = 0;
+    for (int32_t b = 0; b < nb; ++b) used += a->refcount[b] > 0;
+    // Used blocks at or above `used` pair, in increasing order, with the free
+    // blocks below it; the two lists have equal length.
+    std::vector<int32_t> remap(static_cast<size_t>(nb));
+    for (int32_t b = 0; b < nb; ++b) remap[b] = b;
+    int32_t moves = 0, hole = 0;
+    for (int32_t b = used; b < nb; ++b) {
+        if (a->refcount[b] == 0) continue;
+        while (a->refcount[hole] != 0) ++hole;
+        remap[b] = hole++;
+        ++moves;
+    }
+    *n_pairs = moves;
+    if (moves > max_pairs)
+        return fail(PA_ERR_RANGE, "pa_alloc_compact: %d moves, room for %d", moves, max_pairs);
+    if (moves > 0 && !pairs_out) return fail(PA_ERR_NULL, "pa_alloc_compact: pairs_out is NULL");
+    int32_t k = 0;
+    for (int32_t b = used; b < nb; ++b) {
+        if (remap[b] == b) continue;
+        pairs_out[2 * k] = b;
+        pairs_out[2 * k + 1] = remap[b];
+        ++k;
+        a->refcount[remap[b]] = a->refcount[b];
+        a->refcount[b] = 0;
+    }
+    if (moves > 0) {
+        for (auto& kv : a->seqs)
+            for (int32_t& b : kv.second.blocks) b = remap[b];
+        std::unordered_map<int32_t, CachedKey> cached;
+        cached.reserve(a->cached.size());
+        for (auto& kv : a->cached) {
+            CachedKey key = std::move(kv.second);
+            if (key.parent >= 0) key.parent = remap[key.parent];
+            cached.emplace(remap[kv.first], std::move(key));
+        }
+        a->cached = std::move(cached);
+        for (auto& kv : a->prefix_index) kv.second = remap[kv.second];
+    }
+    a->free_list = FreeList(nb);       // rebuilt in increasing order even with no moves
+    for (int32_t b = used; b < nb; ++b) a->free_list.push_back(b);
+    return ok();
+}
+
+pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* queried_tokens, int64_t* hit_tokens,
+                                int32_t* cached_blocks) {
+    if (!a || !queried_tokens || !hit_tokens || !cached_blocks)
+        return fail(PA_ERR_NULL, "pa_alloc_prefix_stats: NULL argument");
+    *queried_tokens = a->prefix_queried;
+    *hit_tokens = a->prefix_hits;
+    *cached_blocks = static_cast<int32_t>(a->prefix_index.size());
     return ok();
 }
 

@@ -5,7 +5,7 @@
 // each new token's key and value rows are written to the cache slot named by
 // a per-token slot mapping, with the cache seen as a flat array of slots.
 //
-// Design: one token row (num_kv_heads * head_dim fp16, contiguous in both the
+// Design (store): one token row (num_kv_heads * head_dim fp16, contiguous in both the
 // input and the slot-major cache) is moved as 16-byte words.  grid.x walks
 // tokens, grid.y splits a row over 256-lane workgroups so that a large row
 // (8 KiB for 32 heads x 128) still spreads over several CUs.  The data never
@@ -32,20 +32,49 @@ __global__ __launch_bounds__(256) void store_kvcache_kernel(
     v_cache[dst] = vw;
 }
 
+// Block copy.  A workgroup moves one tile of kCopyUnroll * 256 16-byte words
+// of one pair, in both caches: every lane issues all of its K and V loads
+// before its first store, so 8 loads per lane are in flight.  The caches are
+// far larger than L2 and the copied block is not read back soon, so loads and
+// stores bypass it (non-temporal).
+constexpr int kCopyUnroll = 4;
+constexpr int64_t kCopyTile = 256 * kCopyUnroll;
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
-    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
-    const int32_t* __restrict__ pairs, int64_t block_vec16, int32_t num_blocks) {
-    const int32_t src = pairs[2 * blockIdx.x];
-    const int32_t dst = pairs[2 * blockIdx.x + 1];
+    u4* __restrict__ k_cache, u4* __restrict__ v_cache, const int32_t* __restrict__ pairs,
+    int64_t block_vec16, int32_t num_blocks, int32_t tiles_per_block) {
+    const int32_t pair = blockIdx.x / tiles_per_block;
+    const int32_t tile = blockIdx.x - pair * tiles_per_block;
+    const int32_t src = pairs[2 * pair];
+    const int32_t dst = pairs[2 * pair + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-    const size_t s0 = static_cast<size_t>(src) * block_vec16;
-    const size_t d0 = static_cast<size_t>(dst) * block_vec16;
-    for (int64_t i = static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x; i < block_vec16;
-         i += static_cast<int64_t>(gridDim.y) * 256) {
-        const uint4 kw = k_cache[s0 + i];
-        const uint4 vw = v_cache[s0 + i];
-        k_cache[d0 + i] = kw;
-        v_cache[d0 + i] = vw;
+    const int64_t base = tile * kCopyTile + threadIdx.x;
+    const u4* ks = k_cache + src * block_vec16;
+    const u4* vs = v_cache + src * block_vec16;
+    u4* kd = k_cache + dst * block_vec16;
+    u4* vd = v_cache + dst * block_vec16;
+    u4 kw[kCopyUnroll], vw[kCopyUnroll];
+    if (base + (kCopyUnroll - 1) * 256 < block_vec16) {
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            kw[u] = __builtin_nontemporal_load(ks + base + u * 256);
+            vw[u] = __builtin_nontemporal_load(vs + base + u * 256);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            __builtin_nontemporal_store(kw[u], kd + base + u * 256);
+            __builtin_nontemporal_store(vw[u], vd + base + u * 256);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t i = base + u * 256;
+            if (i < block_vec16) {
+                kd[i] = ks[i];
+                vd[i] = vs[i];
+            }
+        }
     }
 }
 
@@ -67,12 +96,12 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
                               int32_t num_pairs, int64_t block_vec16, int32_t num_blocks,
                               hipStream_t stream) {
     if (num_pairs <= 0) return hipSuccess;
-    int64_t ys = (block_vec16 + 255) / 256;
-    if (ys > 64) ys = 64;
-    dim3 grid(static_cast<unsigned>(num_pairs), static_cast<unsigned>(ys));
-    hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream,
-                       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), pairs,
-                       block_vec16, num_blocks);
+    const int64_t tiles = (block_vec16 + kCopyTile - 1) / kCopyTile;
+    const int64_t grid = tiles * num_pairs;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                       static_cast<u4*>(k_cache), static_cast<u4*>(v_cache), pairs, block_vec16,
+                       num_blocks, static_cast<int32_t>(tiles));
     return hipGetLastError();
 }
 

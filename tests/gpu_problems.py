@@ -39,7 +39,7 @@ def plans(wl, plan_fn=None):
     assert list(p_dev.context_lens) == list(p_ref.context_lens)
     assert list(p_dev.step_slots) == list(p_ref.step_slots)
     assert [tuple(c) for c in p_dev.cow_pairs] == [tuple(c) for c in p_ref.cow_pairs]
-    return cpp, p_dev, p_ref
+    return cpp, model, p_dev, p_ref
 
 
 def used_slot_mask(wl, tables, lens):
@@ -64,7 +64,7 @@ def build(wl, plan_fn=None, fill="sentinel", store_prior=True):
           oracle); "random" -> every slot starts N(0,1), then slots that hold
           no token of the step's context are overwritten with NaN patterns.
     """
-    cpp, p_dev, p_ref = plans(wl, plan_fn)
+    cpp, model, p_dev, p_ref = plans(wl, plan_fn)
     shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
     hkv, d = wl.num_kv_heads, wl.head_dim
     if fill == "sentinel":
@@ -103,7 +103,7 @@ def build(wl, plan_fn=None, fill="sentinel", store_prior=True):
     cows = torch.tensor([list(c) for c in p_dev.cow_pairs], dtype=torch.int32,
                         device=DEV).reshape(-1, 2)
     return {
-        "wl": wl, "alloc": cpp, "plan": p_dev,
+        "wl": wl, "alloc": cpp, "model": model, "plan": p_dev,
         "kc": kc, "vc": vc, "q": q, "k_new": k_new, "v_new": v_new,
         "tables": tables, "lens": lens, "slots": slots, "cows": cows,
         "max_ctx": int(max(p_dev.context_lens)) if B else 0,
