@@ -19,17 +19,20 @@ Modules
 -------
 store          raw-bit scatter through ``slot_mapping`` and whole-block copies.
 attention      gather through block tables + dense softmax attention (fp64).
+prefill        causal attention of packed prompt chunks over the same cache.
 splitk         the same attention computed over token chunks and recombined.
 bruteforce     a second, scalar-loop coding of ``attention`` for tiny inputs.
 allocator_model  free list, reference counts, fork and copy-on-write,
                content-hash prefix caching and compaction.
 
 Pin status: every function here is pinned by a ``-m "not gpu"`` test in
-``tests/test_oracle.py`` or ``tests/test_allocator_model.py``.
+``tests/test_oracle.py``, ``tests/test_oracle_prefill.py``,
+``tests/test_allocator_model.py`` or ``tests/test_prefix_compact_model.py``.
 """
 
 from .store import store_ref, copy_blocks_ref
 from .attention import gather_sequence, decode_ref
+from .prefill import prefill_ref
 from .splitk import decode_splitk_ref
 from .bruteforce import decode_bruteforce, store_bruteforce
 from .allocator_model import AllocatorModel, AllocError, block_hash, fnv1a64
@@ -39,6 +42,7 @@ __all__ = [
     "copy_blocks_ref",
     "gather_sequence",
     "decode_ref",
+    "prefill_ref",
     "decode_splitk_ref",
     "decode_bruteforce",
     "store_bruteforce",
