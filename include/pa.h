@@ -194,6 +194,48 @@ int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads,
                              int32_t num_splits);
 
 /* ----------------------------------------------------------------------- */
+/* Chunked prefill: causal attention of packed prompt chunks over the cache.
+ *
+ * Sources: [PA-mem] "Deployable configuration parameters" (prompts are
+ * prefilled in chunks, 256 tokens); [vLLM-core] section 3 ("Continuous
+ * batching": one batch carries the prefill of several requests); [nano-KV]
+ * "Engineering: configuration and monitoring" (prefill attention is a
+ * variable-length routine whose plain fallback is standard attention).
+ *
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1 (n_s rows):
+ * the last n_s tokens of its context of L = context_lens[s] tokens, whose K
+ * and V must already be in the caches (pa_store_kvcache).  Row j (KV head
+ * g = h / (num_q_heads / num_kv_heads) for query head h) computes
+ *     z_p = scale * dot(q[row][h], K[s, p, g])     p = 0 .. L - n_s + j
+ *     out[row][h] = sum_p softmax(z)_p * V[s, p, g]
+ * with K/V reached through the block table as in pa_decode.  Products and
+ * sums are fp32 (matrix cores); the probabilities enter the second product
+ * rounded to fp16; the output is rounded to fp16 (nearest even) once.
+ *
+ *   q, out         device fp16 [num_tokens][num_q_heads][head_dim]
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   device int32 [num_seqs], each in [n_s, max_context_len]
+ *                  and at most max_blocks_per_seq * block_size
+ *   query_start    device int32 [num_seqs + 1], from 0 to num_tokens, not
+ *                  decreasing
+ *   max_query_len  at least every n_s: it sizes the grid, and rows past it
+ *                  are not written
+ *   scale          positive and finite
+ *
+ * head_dim 64 or 128; any block_size; any group size.  Lengths are clamped
+ * on the device so that nothing outside the buffers is read; an out-of-range
+ * table entry reads as zero rows (the result of rows that see it is then
+ * unspecified).  PA_VALIDATE checks all of this on the host first.  No
+ * workspace; enqueued on hip_stream.
+ */
+pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
+                     const pa_cache_desc* cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+                     float scale, void* out, void* hip_stream);
+
+/* ----------------------------------------------------------------------- */
 /* Host-side block allocator (the block manager).
  *
  * Sources: [PA-mem] "PagedAttention: the operating system's memory wisdom"

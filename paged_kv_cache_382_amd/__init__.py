@@ -17,7 +17,7 @@ import numpy as np
 
 __all__ = [
     "PaError", "CacheDesc", "lib",
-    "pa_store_kvcache", "pa_copy_blocks", "pa_decode",
+    "pa_store_kvcache", "pa_copy_blocks", "pa_decode", "pa_prefill",
     "pa_decode_workspace_bytes", "pa_decode_num_splits",
     "pa_set_validate", "pa_version", "Allocator", "decode_workspace", "DecodeStepGraph",
 ]
@@ -70,6 +70,8 @@ SIGNATURES = {
                                  _I32, ctypes.c_float, _P, _I32, _P, ctypes.c_size_t, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32]),
     "pa_decode_num_splits": (_I32, [ctypes.POINTER(CacheDesc), _I32, _I32]),
+    "pa_prefill": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P, _P, _I32,
+                                  _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P]),
     "pa_alloc_create": (ctypes.c_int, [_I32, _I32, _I32, _PI32, ctypes.POINTER(_P)]),
     "pa_alloc_destroy": (None, [_P]),
     "pa_alloc_add_seq": (ctypes.c_int, [_P, _I64, _I32, _PI32]),
@@ -235,6 +237,40 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         _dev(context_lens, torch.int32, "context_lens"), B, hq, int(max_context_len),
         float(scale), _dev(out, torch.float16, "out"), int(num_splits), ws_ptr, ws_bytes,
         _stream(stream)))
+    return out
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out=None,
+               max_query_len=None, max_context_len=None, stream=None):
+    """Causal attention of packed prompt chunks; returns ``out`` [T, Hq, D] fp16.
+
+    ``query_start`` (device int32 [B + 1]) splits the T rows of ``q`` into the
+    sequences' chunks; each chunk is the last rows of its sequence's context
+    (``context_lens``), already stored in the caches.  ``max_query_len`` (host
+    int, at least every chunk's length) is read from ``query_start`` when not
+    given, which synchronises; ``max_context_len`` defaults to the table
+    width times the block size.
+    """
+    import torch
+    desc = cache_desc(k_cache)
+    T, hq, d = q.shape
+    B, M = block_tables.shape
+    if context_lens.numel() != B or query_start.numel() != B + 1:
+        raise ValueError("context_lens must be [B] and query_start [B + 1]")
+    if max_query_len is None:
+        qs = query_start.to("cpu", torch.int64)
+        max_query_len = int((qs[1:] - qs[:-1]).max().item()) if B else 0
+    if max_context_len is None:
+        max_context_len = M * desc.block_size
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().pa_prefill(
+        _dev(q, torch.float16, "q"), _dev(k_cache, torch.float16, "k_cache"),
+        _dev(v_cache, torch.float16, "v_cache"), ctypes.byref(desc),
+        _dev(block_tables, torch.int32, "block_tables"), M,
+        _dev(context_lens, torch.int32, "context_lens"),
+        _dev(query_start, torch.int32, "query_start"), B, T, hq, int(max_query_len),
+        int(max_context_len), float(scale), _dev(out, torch.float16, "out"), _stream(stream)))
     return out
 
 

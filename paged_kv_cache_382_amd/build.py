@@ -36,6 +36,7 @@ SOURCES = [
     ("capi.cpp", "hip-host"),
     ("store_kvcache.hip", "hip"),
     ("decode.hip", "hip"),
+    ("prefill.hip", "hip"),
 ]
 
 

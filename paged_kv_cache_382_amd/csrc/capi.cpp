@@ -288,4 +288,82 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     return ok();
 }
 
+pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
+                     const pa_cache_desc* cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+                     float scale, void* out, void* hip_stream) {
+    static const char* fn = "pa_prefill";
+    pa_status st = pa::check_cache(cache, fn);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || max_query_len < 0 || max_context_len < 0)
+        return fail(PA_ERR_SHAPE, "%s: negative size or num_q_heads <= 0", fn);
+    if (num_q_heads % cache->num_kv_heads != 0)
+        return fail(PA_ERR_SHAPE, "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
+                    num_q_heads, cache->num_kv_heads);
+    if (!pa::prefill_supported(cache->head_dim))
+        return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, cache->head_dim);
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
+    if (!(scale > 0.0f) || scale > 1e30f) return fail(PA_ERR_RANGE, "%s: scale must be positive and finite", fn);
+    if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+        return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+    if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
+        return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
+    const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
+                                                   max_context_len);
+    const int64_t rows = static_cast<int64_t>(max_query_len) * (num_q_heads / cache->num_kv_heads);
+    if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads * ((rows + 127) / 128) > INT32_MAX / 2)
+        return fail(PA_ERR_SHAPE, "%s: launch too large", fn);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (pa::validate_flag()) {
+        std::vector<int32_t> lens, starts, tables;
+        st = pa::fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
+        if (st == PA_OK) st = pa::fetch(query_start, static_cast<size_t>(num_seqs) + 1, starts, stream, fn);
+        if (st == PA_OK)
+            st = pa::fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
+        if (st != PA_OK) return st;
+        if (starts[0] != 0 || starts[num_seqs] != num_tokens)
+            return fail(PA_ERR_RANGE, "%s: query_start must run from 0 to num_tokens (%d)", fn, num_tokens);
+        for (int32_t s = 0; s < num_seqs; ++s) {
+            const int32_t n = starts[s + 1] - starts[s], L = lens[s];
+            if (n < 0) return fail(PA_ERR_RANGE, "%s: query_start decreases at %d", fn, s);
+            if (n > max_query_len)
+                return fail(PA_ERR_RANGE, "%s: chunk %d has %d rows > max_query_len %d", fn, s, n, max_query_len);
+            if (L < n || L > max_tokens64)
+                return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [%d, %lld]", fn, s, L, n,
+                            (long long)max_tokens64);
+            const int32_t used = (L + cache->block_size - 1) / cache->block_size;
+            for (int32_t j = 0; j < used; ++j) {
+                const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
+                if (b < 0 || b >= cache->num_blocks)
+                    return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
+            }
+        }
+    }
+    pa::PrefillArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start = query_start;
+    a.out = static_cast<uint16_t*>(out);
+    a.num_blocks = cache->num_blocks;
+    a.block_size = cache->block_size;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.head_dim = cache->head_dim;
+    a.num_q_heads = num_q_heads;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_tokens = static_cast<int32_t>(max_tokens64);
+    a.max_query_len = max_query_len;
+    a.scale_log2 = scale * pa::kLog2e;
+    hipError_t err = pa::launch_prefill(a, stream);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return ok();
+}
+
 }  // extern "C"

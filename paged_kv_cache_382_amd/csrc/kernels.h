@@ -36,6 +36,32 @@ bool decode_supported(int head_dim, int block_size, int group);
 int decode_resident_workgroups(int head_dim, int block_size, int group);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Arguments of one chunked-prefill call, already checked by the caller.
+struct PrefillArgs {
+    const uint16_t* q;             // fp16 [T][Hq][D], chunk rows of all sequences, packed
+    const uint16_t* k_cache;       // fp16 [NB][BS][Hkv][D]
+    const uint16_t* v_cache;
+    const int32_t* block_tables;   // [B][M]
+    const int32_t* context_lens;   // [B], including the chunk
+    const int32_t* query_start;    // [B + 1]
+    uint16_t* out;                 // fp16 [T][Hq][D]
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t num_q_heads;
+    int32_t num_seqs;
+    int32_t num_tokens;            // T
+    int32_t max_blocks_per_seq;    // M
+    int32_t max_tokens;            // M * BS, clamp of context lengths
+    int32_t max_query_len;         // bound on every chunk length (grid size)
+    int32_t tiles_per_seq;         // set by the launcher
+    float scale_log2;              // scale * log2(e), > 0
+};
+
+bool prefill_supported(int head_dim);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 hipError_t launch_store_kvcache(const void* k, const void* v, const int32_t* slots,
                                 int32_t num_tokens, void* k_cache, void* v_cache,
                                 int32_t row_vec16, int64_t total_slots, hipStream_t stream);

@@ -113,3 +113,38 @@ def test_workspace_and_split_queries():
     assert pa.pa_decode_workspace_bytes(d, 4, 32, 0) == (n + 32) * 4 * (2 + 128) * 4
     assert pa.pa_decode_workspace_bytes(d, 4, 33, 0) == 0             # invalid -> 0
     assert pa.pa_decode_num_splits(d, 32, -3) == 0
+
+
+def call_prefill(desc=None, **kw):
+    args = dict(q=0x1000, k=0x2000, v=0x3000, tables=0x4000, M=4, lens=0x5000, starts=0x5800, B=2,
+                T=8, hq=4, max_q=4, max_ctx=64, scale=0.125, out=0x6000)
+    args.update(kw)
+    d = desc if desc is not None else _desc()
+    return pa.lib().pa_prefill(args["q"], args["k"], args["v"], ctypes.byref(d) if d else None,
+                               args["tables"], args["M"], args["lens"], args["starts"], args["B"],
+                               args["T"], args["hq"], args["max_q"], args["max_ctx"], args["scale"],
+                               args["out"], None)
+
+
+@pytest.mark.parametrize("kw,desc,code", [
+    (dict(q=None), None, "NULL"),
+    (dict(starts=None), None, "NULL"),
+    (dict(out=0x6008), None, "ALIGN"),
+    (dict(hq=6), None, "SHAPE"),
+    (dict(T=-1), None, "SHAPE"),
+    (dict(max_q=-1), None, "SHAPE"),
+    (dict(M=0), None, "SHAPE"),
+    (dict(scale=0.0), None, "RANGE"),
+    (dict(scale=-0.5), None, "RANGE"),
+    (dict(scale=float("nan")), None, "RANGE"),
+    (dict(), _desc(d=96), "UNSUPPORTED"),
+    (dict(), _desc(nb=0), "SHAPE"),
+])
+def test_prefill_rejects_bad_arguments(kw, desc, code):
+    assert call_prefill(desc, **kw) == NAMES[code]
+    assert pa.lib().pa_last_error().decode()
+
+
+def test_prefill_empty_batch_is_a_no_op():
+    assert call_prefill(B=0, q=None, out=None) == 0
+    assert call_prefill(T=0, q=None, out=None) == 0

@@ -67,6 +67,13 @@ def long_workload(block_size=16):
 
 
 LONG = long_workload(16)
+# Chunked prefill: every sequence prefills the last chunk (256 tokens, the
+# pages' prefill chunk size) of a 2048-token prompt; MHA and grouped heads.
+PREFILL_CHUNK = 256
+PREFILL_CONTEXT = 2048
+PREFILL_MHA = Workload("prefill_mha", 32, 32, 32, 128, 16, 4160, 128, seed=5)
+PREFILL_GQA = Workload("prefill_gqa", 32, 32, 8, 128, 16, 4160, 128, seed=6)
+PREFILLS = {w.name: w for w in (PREFILL_MHA, PREFILL_GQA)}
 ALL = {w.name: w for w in (TINY, MHA, MIX, PREFIX, LONG)}
 
 TINY_LENS = (1, 7, 16, 33)
