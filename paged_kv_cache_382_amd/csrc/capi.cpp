@@ -302,8 +302,9 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
     if (num_q_heads % cache->num_kv_heads != 0)
         return fail(PA_ERR_SHAPE, "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
                     num_q_heads, cache->num_kv_heads);
-    if (!pa::prefill_supported(cache->head_dim))
-        return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, cache->head_dim);
+    if (!pa::prefill_supported(cache->head_dim, cache->block_size))
+        return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d / block_size %d not supported (64 or 128; a power of two)",
+                    fn, cache->head_dim, cache->block_size);
     if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
     if (!(scale > 0.0f) || scale > 1e30f) return fail(PA_ERR_RANGE, "%s: scale must be positive and finite", fn);
     if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
@@ -360,6 +361,8 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_tokens = static_cast<int32_t>(max_tokens64);
     a.max_query_len = max_query_len;
+    a.block_shift = 0;
+    while ((1 << a.block_shift) < cache->block_size) ++a.block_shift;
     a.scale_log2 = scale * pa::kLog2e;
     hipError_t err = pa::launch_prefill(a, stream);
     if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));

@@ -56,10 +56,11 @@ struct PrefillArgs {
     int32_t max_tokens;            // M * BS, clamp of context lengths
     int32_t max_query_len;         // bound on every chunk length (grid size)
     int32_t tiles_per_seq;         // set by the launcher
+    int32_t block_shift;           // log2(block_size)
     float scale_log2;              // scale * log2(e), > 0
 };
 
-bool prefill_supported(int head_dim);
+bool prefill_supported(int head_dim, int block_size);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_store_kvcache(const void* k, const void* v, const int32_t* slots,

@@ -17,12 +17,13 @@
 // Design.  The packed query rows of one (sequence, KV head) are r = j*G + h'
 // (token-major, then the G query heads that share the KV head), so grouped
 // heads become extra rows of one contraction and every K/V row read from HBM
-// serves all G heads.  A workgroup of kWaves waves owns 32*kWaves rows, 32 a
-// wave.  For each tile of KT keys:
+// serves all G heads.  A workgroup of kWaves waves owns 32*kNT*kWaves rows,
+// 32*kNT a wave.  For each tile of KT keys:
 //   * the workgroup stages K (row-major, rows padded to D*2+16 bytes) and V
-//     (transposed, [d][slot], slot = key with bits 2 and 3 swapped) in LDS;
-//     the next tile's global loads are issued before the current tile is
-//     consumed;
+//     (transposed, [d][slot], slot = key with bits 2 and 3 swapped) in one of
+//     two LDS buffers; while tile t is consumed, tile t+1 is written to the
+//     other buffer, tile t+2's global loads are in flight and tile t+3's
+//     block ids are being fetched, so there is one barrier per tile;
 //   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_f16 (A = K from
 //     LDS, B = Q held in registers), so that a lane owns one query row
 //     (column l % 32) and 16 keys of each 32-key sub-tile;
@@ -34,6 +35,8 @@
 //     accumulators as the B operand: accumulator register r of a 32-key
 //     sub-tile holds key (r/4)*8 + 4*(l/32) + r%4, which is MFMA k-slot
 //     8*(l/32) + r%8 of k-step r/8 once V's keys are stored in slot order.
+// Keys past the context or behind an out-of-range table entry read a safe
+// address; their V rows are zeroed when staged and their scores are masked.
 // The output is normalised once and rounded to fp16 (round to nearest even).
 
 #include "kernels.h"
@@ -66,20 +69,25 @@ __device__ __forceinline__ int work_item(int b, int grid) {
     return (b & 7) * per_xcd + (b >> 3);
 }
 
-template <int D, int KT, int kWaves>
+template <int D, int KT, int kWaves, int kNT>
 __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     constexpr int kThreads = kWaves * 64;
-    constexpr int kRowsWG = 32 * kWaves;
+    constexpr int kRowsWave = 32 * kNT;               // query rows of one wave
+    constexpr int kRowsWG = kRowsWave * kWaves;
     constexpr int kKRow = D * 2 + 16;                 // bytes per K row in LDS
     constexpr int kVRow = KT * 2 + 16;                // bytes per V^T row in LDS
     constexpr int kChunks = D / 8;                    // 16-byte pieces of a row
-    constexpr int kKLoads = (KT * kChunks + kThreads - 1) / kThreads;
-    constexpr int kVLoads = (KT / 2 * kChunks + kThreads - 1) / kThreads;
+    constexpr int kKPieces = KT * kChunks;
+    constexpr int kVPieces = KT / 2 * kChunks;        // (key pair, piece) units
+    constexpr int kKLoads = (kKPieces + kThreads - 1) / kThreads;
+    constexpr int kVLoads = (kVPieces + kThreads - 1) / kThreads;
     constexpr int kSub = KT / 32;                     // 32-key sub-tiles per tile
     constexpr int kDT = D / 32;                       // 32-wide output column tiles
     constexpr int kQS = D / 16;                       // k-steps of the QK contraction
-    __shared__ __align__(16) unsigned char lds_k[KT * kKRow];
-    __shared__ __align__(16) unsigned char lds_v[D * kVRow];
+    constexpr int kKBytes = KT * kKRow;
+    constexpr int kBuf = kKBytes + D * kVRow;         // one K + V^T stage
+    static_assert(kKPieces % 64 == 0 && kVPieces % 64 == 0, "whole waves per load slot");
+    __shared__ __align__(16) unsigned char lds[2 * kBuf];
 
     const int G = a.num_q_heads / a.num_kv_heads;
     const int items = a.num_seqs * a.num_kv_heads * a.tiles_per_seq;
@@ -106,206 +114,257 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     const int lane = tid & 63;
     const int m = lane & 31;
     const int hi = lane >> 5;
-    const int my_row = row0 + wave * 32 + m;
-    const bool row_ok = my_row < rows;
-    const int r_eff = row_ok ? my_row : rows - 1;
-    const int j = r_eff / G;
-    const int hq = g * G + (r_eff - j * G);
     const int first = L - n;                          // position of chunk row 0
-    const int pos = first + j;
 
-    // Key range of this wave and of the whole workgroup.
-    const int w_row_lo = row0 + wave * 32;
+    const int w_row_lo = row0 + wave * kRowsWave;
     const bool wave_on = w_row_lo < rows;
-    const int w_row_hi = min(w_row_lo + 31, rows - 1);
+    const int w_row_hi = min(w_row_lo + kRowsWave - 1, rows - 1);
     const int w_pos_lo = first + w_row_lo / G;
     const int w_pos_hi = first + w_row_hi / G;
-    const int g_pos_hi = first + (min(row0 + kRowsWG, rows) - 1) / G;
-    const int n_keys = g_pos_hi + 1;
+    const int n_keys = first + (min(row0 + kRowsWG, rows) - 1) / G + 1;
     const int n_tiles = (n_keys + KT - 1) / KT;
 
-    // Q^T operand: row r_eff, dims 16*ks + 8*hi .. +8.
-    h8 qv[kQS];
-    {
-        const _Float16* qp = reinterpret_cast<const _Float16*>(a.q) +
-                             (static_cast<size_t>(qs + j) * a.num_q_heads + hq) * D + 8 * hi;
+    // Rows of this lane (one per 32-row group) and their Q^T operands.
+    int row_tok[kNT], row_head[kNT], row_pos[kNT];
+    bool row_ok[kNT];
+    h8 qv[kNT][kQS];
 #pragma unroll
-        for (int ks = 0; ks < kQS; ++ks) qv[ks] = *reinterpret_cast<const h8*>(qp + 16 * ks);
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int r = w_row_lo + 32 * nt + m;
+        row_ok[nt] = r < rows;
+        const int re = row_ok[nt] ? r : rows - 1;
+        const int jj = re / G;
+        row_tok[nt] = qs + jj;
+        row_head[nt] = g * G + (re - jj * G);
+        row_pos[nt] = first + jj;
+        const _Float16* qp = reinterpret_cast<const _Float16*>(a.q) +
+                             (static_cast<size_t>(row_tok[nt]) * a.num_q_heads + row_head[nt]) * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < kQS; ++ks) qv[nt][ks] = *reinterpret_cast<const h8*>(qp + 16 * ks);
     }
 
-    const int bs = a.block_size;
+    const int bshift = a.block_shift;
+    const int bmask = (1 << bshift) - 1;
     const int* table = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
-    const size_t head_off = static_cast<size_t>(g) * D;
-    const size_t slot_stride = static_cast<size_t>(a.num_kv_heads) * D;
-    const u4 zero4 = {0u, 0u, 0u, 0u};
+    const size_t row_stride = static_cast<size_t>(a.num_kv_heads) * D;   // halves per slot
+    const uint16_t* kbase = a.k_cache + static_cast<size_t>(g) * D;
+    const uint16_t* vbase = a.v_cache + static_cast<size_t>(g) * D;
 
-    // Global address of (key, 16-byte piece c), or null when the key holds no
-    // token (past the context, or an out-of-range table entry).
-    auto row_ptr = [&](const uint16_t* cache, int key, int c) -> const u4* {
-        if (key >= L) return nullptr;
-        const int blk = table[key / bs];
-        if (blk < 0 || blk >= a.num_blocks) return nullptr;
-        const size_t slot = static_cast<size_t>(blk) * bs + key % bs;
-        return reinterpret_cast<const u4*>(cache + slot * slot_stride + head_off + 8 * c);
-    };
+    // This thread's fixed key offsets inside a tile: K piece slots and V pairs.
+    int koff[kKLoads], kpiece[kKLoads], voff[kVLoads], vpiece[kVLoads];
+#pragma unroll
+    for (int u = 0; u < kKLoads; ++u) {
+        const int idx = min(tid + u * kThreads, kKPieces - 1);
+        koff[u] = idx / kChunks;
+        kpiece[u] = idx % kChunks;
+    }
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) {
+        const int idx = min(tid + u * kThreads, kVPieces - 1);
+        voff[u] = 2 * (idx % (KT / 2));
+        vpiece[u] = idx / (KT / 2);
+    }
 
-    u4 kreg[kKLoads];
-    u4 vreg[kVLoads][2];
-    auto load_tile = [&](int k0) {
+    // Block ids of the tile after the one being loaded (one tile ahead).
+    int kblk[kKLoads], vblk[kVLoads][2];
+    auto fetch_ids = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < kKLoads; ++u) {
-            const int idx = tid + u * kThreads;
-            kreg[u] = zero4;
-            if (idx < KT * kChunks) {
-                const u4* p = row_ptr(a.k_cache, k0 + idx / kChunks, idx % kChunks);
-                if (p) kreg[u] = *p;
-            }
+            const int key = k0 + koff[u];
+            kblk[u] = key < L ? table[key >> bshift] : -1;
         }
 #pragma unroll
-        for (int u = 0; u < kVLoads; ++u) {
-            const int idx = tid + u * kThreads;
-            vreg[u][0] = zero4;
-            vreg[u][1] = zero4;
-            if (idx < KT / 2 * kChunks) {
-                const int kp = idx % (KT / 2);
-                const int c = idx / (KT / 2);
-                const u4* p0 = row_ptr(a.v_cache, k0 + 2 * kp, c);
-                const u4* p1 = row_ptr(a.v_cache, k0 + 2 * kp + 1, c);
-                if (p0) vreg[u][0] = *p0;
-                if (p1) vreg[u][1] = *p1;
+        for (int u = 0; u < kVLoads; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int key = k0 + voff[u] + e;
+                vblk[u][e] = key < L ? table[key >> bshift] : -1;
             }
-        }
     };
-    auto store_tile = [&]() {
+    // Global loads of one tile into registers; a key that holds no token (past
+    // the context, or an out-of-range block) reads a safe address and its V
+    // piece is zeroed when staged.
+    u4 kreg[kKLoads], vreg[kVLoads][2];
+    unsigned vvalid = 0;
+    auto issue_tile = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < kKLoads; ++u) {
-            const int idx = tid + u * kThreads;
-            if (idx < KT * kChunks)
-                *reinterpret_cast<u4*>(lds_k + (idx / kChunks) * kKRow + (idx % kChunks) * 16) = kreg[u];
+            const int key = k0 + koff[u];
+            const int b = kblk[u];
+            const bool ok = b >= 0 && b < a.num_blocks;
+            const size_t slot = ok ? (static_cast<size_t>(b) << bshift) + (key & bmask) : 0;
+            kreg[u] = *reinterpret_cast<const u4*>(kbase + slot * row_stride + 8 * kpiece[u]);
         }
+        vvalid = 0;
+#pragma unroll
+        for (int u = 0; u < kVLoads; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int key = k0 + voff[u] + e;
+                const int b = vblk[u][e];
+                const bool ok = b >= 0 && b < a.num_blocks;
+                const size_t slot = ok ? (static_cast<size_t>(b) << bshift) + (key & bmask) : 0;
+                vreg[u][e] = *reinterpret_cast<const u4*>(vbase + slot * row_stride + 8 * vpiece[u]);
+                vvalid |= (ok ? 1u : 0u) << (2 * u + e);
+            }
+    };
+    auto stage_tile = [&](unsigned char* buf) {
+#pragma unroll
+        for (int u = 0; u < kKLoads; ++u)
+            if (tid + u * kThreads < kKPieces)
+                *reinterpret_cast<u4*>(buf + koff[u] * kKRow + kpiece[u] * 16) = kreg[u];
+        unsigned char* vt = buf + kKBytes;
 #pragma unroll
         for (int u = 0; u < kVLoads; ++u) {
-            const int idx = tid + u * kThreads;
-            if (idx < KT / 2 * kChunks) {
-                const int kp = idx % (KT / 2);
-                const int c = idx / (KT / 2);
-                const int key = 2 * kp;
-                const int col = (key & ~31) + v_slot(key & 31);
-                unsigned char* base = lds_v + (8 * c) * kVRow + col * 2;
+            if (tid + u * kThreads >= kVPieces) continue;
+            const int col = (voff[u] & ~31) + v_slot(voff[u] & 31);
+            unsigned char* base = vt + (8 * vpiece[u]) * kVRow + col * 2;
+            const bool ok0 = (vvalid >> (2 * u)) & 1u, ok1 = (vvalid >> (2 * u + 1)) & 1u;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const unsigned w0 = vreg[u][0][i], w1 = vreg[u][1][i];
-                    // d = 8c + 2i and 8c + 2i + 1: (key, key+1) pairs
-                    *reinterpret_cast<unsigned*>(base + (2 * i) * kVRow) =
-                        (w0 & 0xFFFFu) | (w1 << 16);
-                    *reinterpret_cast<unsigned*>(base + (2 * i + 1) * kVRow) =
-                        (w0 >> 16) | (w1 & 0xFFFF0000u);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const unsigned w0 = ok0 ? vreg[u][0][i] : 0u;
+                const unsigned w1 = ok1 ? vreg[u][1][i] : 0u;
+                // dims 8c + 2i and 8c + 2i + 1, keys (key, key + 1)
+                *reinterpret_cast<unsigned*>(base + (2 * i) * kVRow) = (w0 & 0xFFFFu) | (w1 << 16);
+                *reinterpret_cast<unsigned*>(base + (2 * i + 1) * kVRow) = (w0 >> 16) | (w1 & 0xFFFF0000u);
             }
         }
     };
 
-    f16x acc_o[kDT];
+    f16x acc_o[kNT][kDT];
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.0f;
-    float m_ref = kNegBig;                            // reference max (log2 units)
-    float l_sum = 0.0f;                               // this half-wave's keys only
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_o[nt][dt][r] = 0.0f;
+    float m_ref[kNT], l_sum[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        m_ref[nt] = kNegBig;                          // reference max (log2 units)
+        l_sum[nt] = 0.0f;                             // this half-wave's keys only
+    }
     const float c_log2 = a.scale_log2;
 
-    load_tile(0);
+    // Prologue: stage tile 0, put tile 1 in flight, fetch the ids of tile 2.
+    fetch_ids(0);
+    issue_tile(0);
+    fetch_ids(KT);
+    stage_tile(lds);
+    if (n_tiles > 1) issue_tile(KT);
+    fetch_ids(2 * KT);
+    __syncthreads();
+
     for (int t = 0; t < n_tiles; ++t) {
         const int k0 = t * KT;
-        store_tile();
-        __syncthreads();
-        if (t + 1 < n_tiles) load_tile(k0 + KT);
-
+        const unsigned char* kt = lds + (t & 1) * kBuf;
+        const unsigned char* vt = kt + kKBytes;
         if (wave_on && k0 <= w_pos_hi) {
-            // S^T = K Q^T, one 32x32 accumulator per 32-key sub-tile.
-            f16x sacc[kSub];
+            // S^T = K Q^T: each K operand feeds kNT products.
+            f16x sacc[kNT][kSub];
 #pragma unroll
             for (int st = 0; st < kSub; ++st) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[st][r] = 0.0f;
-                const unsigned char* kb = lds_k + (32 * st + m) * kKRow + 16 * hi;
+                for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[nt][st][r] = 0.0f;
+                const unsigned char* kb = kt + (32 * st + m) * kKRow + 16 * hi;
 #pragma unroll
                 for (int ks = 0; ks < kQS; ++ks) {
                     const h8 kv = *reinterpret_cast<const h8*>(kb + 32 * ks);
-                    sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qv[ks], sacc[st], 0, 0, 0);
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt)
+                        sacc[nt][st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qv[nt][ks], sacc[nt][st], 0, 0, 0);
                 }
             }
-            // causal mask where the tile reaches past the wave's first row
-            if (k0 + KT - 1 > w_pos_lo) {
+            const bool need_mask = k0 + KT - 1 > w_pos_lo;
+            h8 pb[kNT][2 * kSub];
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                if (need_mask) {
+#pragma unroll
+                    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = k0 + 32 * st + (r >> 2) * 8 + 4 * hi + (r & 3);
+                            if (key > row_pos[nt]) sacc[nt][st][r] = kNegBig;
+                        }
+                }
+                float mx = kNegBig;
+#pragma unroll
+                for (int st = 0; st < kSub; ++st)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nt][st][r]);
+                mx = fmaxf(mx, xor32(mx)) * c_log2;
+                const bool grow = mx > m_ref[nt] + kSlack;
+                if (__ballot(grow)) {
+                    const float m_new = grow ? mx : m_ref[nt];
+                    const float alpha = __builtin_amdgcn_exp2f(m_ref[nt] - m_new);
+                    m_ref[nt] = m_new;
+                    l_sum[nt] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc_o[nt][dt][r] *= alpha;
+                }
+                // probabilities -> fp16 B operands, k-step = (sub-tile, half)
 #pragma unroll
                 for (int st = 0; st < kSub; ++st)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * st + (r >> 2) * 8 + 4 * hi + (r & 3);
-                        if (key > pos) sacc[st][r] = kNegBig;
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[nt][st][r], c_log2, -m_ref[nt]));
+                        l_sum[nt] += p;
+                        pb[nt][2 * st + (r >> 3)][r & 7] = static_cast<_Float16>(p);
                     }
             }
-            float mx = kNegBig;
-#pragma unroll
-            for (int st = 0; st < kSub; ++st)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[st][r]);
-            mx = fmaxf(mx, xor32(mx)) * c_log2;
-            const bool grow = mx > m_ref + kSlack;
-            if (__ballot(grow)) {
-                const float m_new = grow ? mx : m_ref;
-                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-                m_ref = m_new;
-                l_sum *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-            }
-            // probabilities -> fp16 B operands, k-step = (sub-tile, half)
-            h8 pb[2 * kSub];
-#pragma unroll
-            for (int st = 0; st < kSub; ++st)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][r], c_log2, -m_ref));
-                    l_sum += p;
-                    pb[2 * st + (r >> 3)][r & 7] = static_cast<_Float16>(p);
-                }
-            // O^T += V^T P^T
+            // O^T += V^T P^T: each V operand feeds kNT products.
 #pragma unroll
             for (int dt = 0; dt < kDT; ++dt) {
-                const unsigned char* vb = lds_v + (32 * dt + m) * kVRow + 16 * hi;
+                const unsigned char* vb = vt + (32 * dt + m) * kVRow + 16 * hi;
 #pragma unroll
                 for (int ks = 0; ks < 2 * kSub; ++ks) {
                     const h8 vv = *reinterpret_cast<const h8*>(vb + 32 * ks);
-                    acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pb[ks], acc_o[dt], 0, 0, 0);
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt)
+                        acc_o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pb[nt][ks], acc_o[nt][dt], 0, 0, 0);
                 }
+            }
+        }
+        // Stage tile t+1 into the other buffer (last read before the previous
+        // barrier), put tile t+2 in flight, fetch the ids of tile t+3.
+        if (t + 1 < n_tiles) {
+            stage_tile(lds + ((t + 1) & 1) * kBuf);
+            if (t + 2 < n_tiles) {
+                issue_tile(k0 + 2 * KT);
+                fetch_ids(k0 + 3 * KT);
             }
         }
         __syncthreads();
     }
 
-    const float l_tot = l_sum + xor32(l_sum);
-    if (!row_ok) return;
-    const float inv = 1.0f / l_tot;
-    _Float16* op = reinterpret_cast<_Float16*>(a.out) +
-                   (static_cast<size_t>(qs + j) * a.num_q_heads + hq) * D + 4 * hi;
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
+    for (int nt = 0; nt < kNT; ++nt) {
+        const float l_tot = l_sum[nt] + xor32(l_sum[nt]);
+        if (!row_ok[nt]) continue;
+        const float inv = 1.0f / l_tot;
+        _Float16* op = reinterpret_cast<_Float16*>(a.out) +
+                       (static_cast<size_t>(row_tok[nt]) * a.num_q_heads + row_head[nt]) * D + 4 * hi;
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            h4 o;
+        for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = static_cast<_Float16>(acc_o[dt][4 * rq + i] * inv);
-            *reinterpret_cast<h4*>(op + 32 * dt + 8 * rq) = o;
-        }
+            for (int rq = 0; rq < 4; ++rq) {
+                h4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = static_cast<_Float16>(acc_o[nt][dt][4 * rq + i] * inv);
+                *reinterpret_cast<h4*>(op + 32 * dt + 8 * rq) = o;
+            }
+    }
 }
 
-template <int D, int KT, int kWaves>
+template <int D, int KT, int kWaves, int kNT>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     PrefillArgs b = a;
-    constexpr int kRowsWG = 32 * kWaves;
+    constexpr int kRowsWG = 32 * kNT * kWaves;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int64_t rows = static_cast<int64_t>(a.max_query_len) * G;
     b.tiles_per_seq = static_cast<int32_t>((rows + kRowsWG - 1) / kRowsWG);
@@ -313,20 +372,22 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     if (items == 0) return hipSuccess;
     const int64_t grid = (items + 7) / 8 * 8;
     if (grid > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<D, KT, kWaves>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((prefill_kernel<D, KT, kWaves, kNT>), dim3(static_cast<unsigned>(grid)),
                        dim3(kWaves * 64), 0, stream, b);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool prefill_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
+bool prefill_supported(int head_dim, int block_size) {
+    return (head_dim == 64 || head_dim == 128) && block_size > 0 && (block_size & (block_size - 1)) == 0;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.num_seqs <= 0 || a.max_query_len <= 0) return hipSuccess;
     switch (a.head_dim) {
-        case 128: return launch_t<128, 32, 4>(a, stream);
-        case 64: return launch_t<64, 64, 4>(a, stream);
+        case 128: return launch_t<128, 64, 8, 1>(a, stream);
+        case 64: return launch_t<64, 64, 8, 1>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
