@@ -16,6 +16,12 @@ HIP events around each call inside the timed region; ``cpu_baseline`` is the
 fp64 CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload mha|mix|prefix|long_bs16|...]
+
+Other modes, each printing its own JSON line: ``--workload prefill_mha`` or
+``prefill_gqa`` (chunked prefill: per layer the store of the chunk's rows and
+causal chunk attention; ``roofline`` against the fp16 matrix peak),
+``--compaction`` (block copies of a compaction plan) and ``--copy-probe``
+(a plain copy of known size, for scaling the HBM byte counters).
 """
 
 import argparse
@@ -33,7 +39,9 @@ import workloads as W
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "pa_decode achieved HBM GB/s (% of MI355X peak) + decode tokens/s, bs32 ctx2048"
 PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E, AMD specification
+PEAK_FP16_TFLOPS = 2500.0        # MI355X dense fp16 matrix peak, AMD specification
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_382_amd", "csrc", "decode.hip")
+PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_382_amd", "csrc", "prefill.hip")
 
 
 # --------------------------------------------------------------------------
@@ -64,6 +72,22 @@ def decode_flops(lens, num_q_heads, head_dim):
     return 4 * sum(int(x) for x in lens) * num_q_heads * head_dim
 
 
+def prefill_flops(context_lens, chunk_lens, num_q_heads, head_dim):
+    """Causal chunk attention: row j of a chunk of n rows in a context of L
+    tokens sees L - n + j + 1 keys; 2 flops a key and dim for Q K^T and 2 for
+    P V, per query head."""
+    keys = 0
+    for L, n in zip(context_lens, chunk_lens):
+        L, n = int(L), int(n)
+        keys += n * (L - n) + n * (n + 1) // 2
+    return 4 * keys * num_q_heads * head_dim
+
+
+def prefill_kv_bytes(context_lens, num_kv_heads, head_dim):
+    """K and V rows of every context token, read once."""
+    return sum(int(L) for L in context_lens) * num_kv_heads * head_dim * 2 * 2
+
+
 def kv_bytes_per_request(layers, hidden, tokens, bytes_per_element=2):
     """K and V of every layer for one request."""
     return 2 * layers * hidden * tokens * bytes_per_element
@@ -87,20 +111,22 @@ def describe(wl, plan):
             f"{wl.layers} layers with distinct caches")
 
 
-def source_digest():
-    with open(DECODE_SRC, "rb") as f:
+def source_digest(path=None):
+    with open(path or DECODE_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counter_traffic(wl_name):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
-    None when the decode kernel source changed since they were taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_{wl_name}_counters.json")
+def counter_traffic(wl_name, kind="decode"):
+    """HBM bytes per launch of the ``kind`` kernel from committed rocprofv3
+    counter runs, or None when that kernel's source changed since they were
+    taken."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{wl_name}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("decode_source_sha256_16") != source_digest():
+    src = DECODE_SRC if kind == "decode" else PREFILL_SRC
+    if rec.get(f"{kind}_source_sha256_16") != source_digest(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -241,6 +267,140 @@ def compaction_probe(wl, dev, reps):
         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}), flush=True)
 
 
+def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s):
+    """The oracle timed on the host: causal rows of the first sequence's
+    chunk, each row being single-query attention over its prefix (the
+    reduction the prefill oracle is pinned to), until ``budget_s`` passes."""
+    import torch
+
+    from oracle import prefill_ref
+    threads = torch.get_num_threads()
+    bs = wl.block_size
+    L = int(lens[0])
+    nb = -(-L // bs)
+    row = np.asarray(tables[0][:nb], dtype=np.int64)
+    k_host = kc[torch.from_numpy(row).to(kc.device)].cpu().numpy()
+    v_host = vc[torch.from_numpy(row).to(vc.device)].cpu().numpy()
+    q_host = q[:chunk].cpu().numpy()
+    local = np.arange(nb, dtype=np.int32)[None, :]
+    done, flops, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < chunk:
+        j = done
+        pos = L - chunk + j
+        prefill_ref(q_host[j:j + 1], k_host, v_host, local, [pos + 1], [0, 1], wl.scale)
+        flops += 4 * (pos + 1) * wl.num_q_heads * wl.head_dim
+        done += 1
+    elapsed = time.perf_counter() - t0
+    return {
+        "value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: {done} causal rows (all {wl.num_q_heads} query heads) "
+                   f"of one sequence's chunk, one layer, in {elapsed:.2f} s"),
+    }
+
+
+def prefill_main(args, wl, dev):
+    """Chunked prefill step: per layer, store the chunk's K/V rows, then causal
+    attention of every chunk row over its context."""
+    import torch
+
+    import paged_kv_cache_382_amd as pa
+    layers = args.layers or wl.layers
+    chunk, ctx = W.PREFILL_CHUNK, W.PREFILL_CONTEXT
+    B, hq, hkv, d, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    alloc = pa.Allocator(wl.num_blocks, bs, wl.max_blocks_per_seq,
+                         W.free_order(wl.num_blocks, wl.seed))
+    slots = []
+    for s in range(B):
+        sl = alloc.add_seq(s, ctx)
+        slots += list(sl[ctx - chunk:])
+    tables_h, lens_h = alloc.export(list(range(B)), wl.max_blocks_per_seq)
+    shape = (wl.num_blocks, bs, hkv, d)
+    caches = []
+    for layer in range(layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(wl.seed * 100000 + layer)
+        caches.append((torch.randn(shape, generator=g, device=dev, dtype=torch.float16),
+                       torch.randn(shape, generator=g, device=dev, dtype=torch.float16)))
+    T = B * chunk
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    q = torch.randn((layers, T, hq, d), generator=g, device=dev, dtype=torch.float16)
+    k_new = torch.randn((layers, T, hkv, d), generator=g, device=dev, dtype=torch.float16)
+    v_new = torch.randn((layers, T, hkv, d), generator=g, device=dev, dtype=torch.float16)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(np.ascontiguousarray(tables_h)).to(dev)
+    lens_d = torch.from_numpy(np.ascontiguousarray(lens_h)).to(dev)
+    starts = torch.arange(0, T + 1, chunk, dtype=torch.int32, device=dev)
+    slots_d = torch.tensor(slots, dtype=torch.int32, device=dev)
+
+    def step(events=None):
+        for layer in range(layers):
+            kc, vc = caches[layer]
+            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots_d, kc, vc)
+            if events is not None:
+                events[layer][0].record()
+            pa.pa_prefill(q[layer], kc, vc, tables, lens_d, starts, wl.scale, out=out[layer],
+                          max_query_len=chunk, max_context_len=ctx)
+            if events is not None:
+                events[layer][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(layers)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        step(events[k])
+    end.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / args.steps
+    pf_ms = float(np.mean([e[0].elapsed_time(e[1]) for row in events for e in row]))
+    lens = [int(x) for x in lens_h]
+    flops = prefill_flops(lens, [chunk] * B, hq, d)
+    value = layers * flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (pf_ms * 1e-3) / 1e12
+    result = {
+        "metric": "chunked-prefill attention TFLOP/s (causal, fp16 in, fp32 accumulate)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: {B} sequences, each prefilling the last {chunk}-token chunk "
+                         f"of a {ctx}-token prompt; {hq}/{hkv} heads, head_dim {d}, block {bs}"),
+            "chunk": chunk, "context": ctx, "layers": layers, "pool_blocks": wl.num_blocks,
+            "parallelism": "single GPU",
+        },
+        "prefill_tokens_per_s": round(T / (step_ms * 1e-3), 1),
+        "prefill_us_per_layer": round(pf_ms * 1e3, 3),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pa_prefill (prefill_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+            "traffic": counter_traffic(wl.name, "prefill"),
+            "flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": prefill_kv_bytes(lens, hkv, d) + 2 * T * hq * d * 2,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(wl, caches[0][0], caches[0][1], q[0],
+                                                      tables_h, lens_h, chunk, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,9 +430,13 @@ def main():
 
     import paged_kv_cache_382_amd as pa
 
+    dev = torch.device("cuda", 0)
+    if args.workload in W.PREFILLS:
+        torch.cuda.set_device(dev)
+        prefill_main(args, W.PREFILLS[args.workload], dev)
+        return
     wl = workload_by_name(args.workload)
     layers = args.layers or wl.layers
-    dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if args.copy_probe:
         copy_probe(wl, dev, max(args.steps, 1))
