@@ -277,6 +277,11 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, sca
 class DecodeStepGraph:
     """One decode step of every layer, captured once into a HIP graph.
 
+    Source: [PA-mem] "Architectural limits and evolution" (graph capture turns
+    many kernel launches into one executable graph) and [nano-KV] "Scheduling
+    strategy and continuous batching" (the token-by-token decode loop is
+    captured as a graph to remove launch and interpreter overhead).
+
     A step is, per layer: the copy-on-write block copies (if any), the store of
     the step's new K/V rows through ``slot_mapping``, and ``pa_decode``.  The
     launches are recorded once; ``replay()`` then issues the whole step with a
