@@ -48,6 +48,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ constexpr h2 kOnes2 = {1.0f16, 1.0f16};
 
 constexpr float kNegBig = -1e30f;
 constexpr float kSlack = 8.0f;        // log2 units: probabilities stay below 2^8
@@ -69,7 +71,7 @@ __device__ __forceinline__ int work_item(int b, int grid) {
     return (b & 7) * per_xcd + (b >> 3);
 }
 
-template <int D, int KT, int kWaves, int kNT>
+template <int D, int KT, int kWaves, int kNT, bool kOff32>
 __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     constexpr int kThreads = kWaves * 64;
     constexpr int kRowsWave = 32 * kNT;               // query rows of one wave
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     const int bshift = a.block_shift;
     const int bmask = (1 << bshift) - 1;
     const int* table = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
-    const size_t row_stride = static_cast<size_t>(a.num_kv_heads) * D;   // halves per slot
+    const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;   // bytes per slot
     const uint16_t* kbase = a.k_cache + static_cast<size_t>(g) * D;
     const uint16_t* vbase = a.v_cache + static_cast<size_t>(g) * D;
 
@@ -181,9 +183,23 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
                 vblk[u][e] = key < L ? table[key >> bshift] : -1;
             }
     };
-    // Global loads of one tile into registers; a key that holds no token (past
-    // the context, or an out-of-range block) reads a safe address and its V
-    // piece is zeroed when staged.
+    // Address of 16-byte piece `piece` of (key, this KV head); a key that holds
+    // no token reads piece `piece` of slot 0 instead.  When every offset of the
+    // cache fits in 32 bits the address is a uniform base plus a 32-bit offset
+    // (scalar-base loads, no 64-bit vector arithmetic).
+    auto piece_ptr = [&](const uint16_t* base, bool ok, int b, int key, int piece) -> const u4* {
+        if constexpr (kOff32) {
+            const uint32_t off = (ok ? ((static_cast<uint32_t>(b) << bshift) + (key & bmask)) * row_bytes : 0u) +
+                                 16u * piece;
+            return reinterpret_cast<const u4*>(reinterpret_cast<const unsigned char*>(base) + off);
+        } else {
+            const size_t slot = ok ? (static_cast<size_t>(b) << bshift) + (key & bmask) : 0;
+            return reinterpret_cast<const u4*>(reinterpret_cast<const unsigned char*>(base) +
+                                               slot * row_bytes + 16u * piece);
+        }
+    };
+    // Global loads of one tile into registers; the V pieces of keys that hold
+    // no token are zeroed when staged.
     u4 kreg[kKLoads], vreg[kVLoads][2];
     unsigned vvalid = 0;
     auto issue_tile = [&](int k0) {
@@ -192,8 +208,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
             const int key = k0 + koff[u];
             const int b = kblk[u];
             const bool ok = b >= 0 && b < a.num_blocks;
-            const size_t slot = ok ? (static_cast<size_t>(b) << bshift) + (key & bmask) : 0;
-            kreg[u] = *reinterpret_cast<const u4*>(kbase + slot * row_stride + 8 * kpiece[u]);
+            kreg[u] = *piece_ptr(kbase, ok, b, key, kpiece[u]);
         }
         vvalid = 0;
 #pragma unroll
@@ -203,8 +218,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
                 const int key = k0 + voff[u] + e;
                 const int b = vblk[u][e];
                 const bool ok = b >= 0 && b < a.num_blocks;
-                const size_t slot = ok ? (static_cast<size_t>(b) << bshift) + (key & bmask) : 0;
-                vreg[u][e] = *reinterpret_cast<const u4*>(vbase + slot * row_stride + 8 * vpiece[u]);
+                vreg[u][e] = *piece_ptr(vbase, ok, b, key, vpiece[u]);
                 vvalid |= (ok ? 1u : 0u) << (2 * u + e);
             }
     };
@@ -313,10 +327,19 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[nt][st][r], c_log2, -m_ref[nt]));
-                        l_sum[nt] += p;
                         pb[nt][2 * st + (r >> 3)][r & 7] = static_cast<_Float16>(p);
                     }
             }
+            // row sums of the fp16 probabilities the products use
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                for (int ks = 0; ks < 2 * kSub; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const h2 pp = {pb[nt][ks][2 * e], pb[nt][ks][2 * e + 1]};
+                        l_sum[nt] = __builtin_amdgcn_fdot2(pp, kOnes2, l_sum[nt], false);
+                    }
             // O^T += V^T P^T: each V operand feeds kNT products.
 #pragma unroll
             for (int dt = 0; dt < kDT; ++dt) {
@@ -363,6 +386,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 
 template <int D, int KT, int kWaves, int kNT>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+    const uint64_t cache_bytes = static_cast<uint64_t>(a.num_blocks) * a.block_size * a.num_kv_heads * D * 2;
     PrefillArgs b = a;
     constexpr int kRowsWG = 32 * kNT * kWaves;
     const int G = a.num_q_heads / a.num_kv_heads;
@@ -372,8 +396,12 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     if (items == 0) return hipSuccess;
     const int64_t grid = (items + 7) / 8 * 8;
     if (grid > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<D, KT, kWaves, kNT>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kWaves * 64), 0, stream, b);
+    if (cache_bytes <= UINT32_MAX)
+        hipLaunchKernelGGL((prefill_kernel<D, KT, kWaves, kNT, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kWaves * 64), 0, stream, b);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, KT, kWaves, kNT, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kWaves * 64), 0, stream, b);
     return hipGetLastError();
 }
 

@@ -149,3 +149,44 @@ def test_prefill_full_size_sampled(name, wl):
             got.append(out[t])
             ref.append(r[0])
     check_close(torch.stack(got), np.stack(ref), f"{name} sampled")
+
+
+def test_prefill_cache_larger_than_4gib():
+    """A pool whose caches exceed 4 GiB, with the sequences' blocks at its top:
+    the kernel must address them with 64-bit offsets.  The oracle runs on a
+    compact host cache built from the same input rows."""
+    hq, hkv, d, bs = 8, 2, 128, 16
+    block_bytes = bs * hkv * d * 2
+    nb = (1 << 32) // block_bytes + 64
+    lens, chunks = [300, 77], [256, 77]
+    order = np.arange(nb - 1, -1, -1, dtype=np.int32)          # highest blocks first
+    alloc = pa.Allocator(nb, bs, 32, order)
+    slots = []
+    for s, L in enumerate(lens):
+        slots += list(alloc.add_seq(s, L))
+    tables, lens_arr = alloc.export([0, 1], 32)
+    assert int(tables[0][0]) * block_bytes >= 1 << 32
+    say(f"prefill: caches of {nb * block_bytes / 2**30:.2f} GiB each")
+    kc = torch.empty((nb, bs, hkv, d), dtype=torch.float16, device=DEV)
+    vc = torch.empty_like(kc)
+    k_rows = W.normal_fp16((len(slots), hkv, d), 71, DEV)
+    v_rows = W.normal_fp16((len(slots), hkv, d), 72, DEV)
+    pa.pa_store_kvcache(k_rows, v_rows, torch.tensor(slots, dtype=torch.int32, device=DEV), kc, vc)
+    starts = np.array([0, 256, 333], dtype=np.int32)
+    q = W.normal_fp16((333, hq, d), 73, DEV)
+    out = pa.pa_prefill(q, kc, vc, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens_arr).to(DEV),
+                        torch.from_numpy(starts).to(DEV), 0.0883883, max_query_len=256)
+    torch.cuda.synchronize()
+    # compact oracle cache: used block i of the tables becomes block i
+    used = sorted({int(b) for row, L in zip(tables, lens_arr) for b in row[:-(-int(L) // bs)]})
+    remap = {b: i for i, b in enumerate(used)}
+    small_tables = np.array([[remap.get(int(b), 0) for b in row] for row in tables], dtype=np.int32)
+    small_slots = [remap[s // bs] * bs + s % bs for s in slots]
+    shape = (len(used), bs, hkv, d)
+    kh, vh = store_ref(host_u16(k_rows).view(np.float16), host_u16(v_rows).view(np.float16), small_slots,
+                       np.zeros(shape, np.uint16), np.zeros(shape, np.uint16))
+    ref = prefill_ref(host_u16(q).view(np.float16), kh.view(np.float16), vh.view(np.float16),
+                      small_tables, lens_arr, starts, 0.0883883)
+    check_close(out, ref, "prefill > 4 GiB pool")
+    del kc, vc
+    torch.cuda.empty_cache()
