@@ -276,21 +276,36 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
         if (wave_on && k0 <= w_pos_hi) {
             // S^T = K Q^T: each K operand feeds kNT products.
             f16x sacc[kNT][kSub];
+            // All K operands of the tile are read from LDS before the first
+            // product, and all V operands right after the last one, so the LDS
+            // latency is paid once a tile and the V reads overlap the softmax.
+            h8 kop[kSub][kQS];
+#pragma unroll
+            for (int st = 0; st < kSub; ++st)
+#pragma unroll
+                for (int ks = 0; ks < kQS; ++ks)
+                    kop[st][ks] = *reinterpret_cast<const h8*>(kt + (32 * st + m) * kKRow + 16 * hi + 32 * ks);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int st = 0; st < kSub; ++st) {
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sacc[nt][st][r] = 0.0f;
-                const unsigned char* kb = kt + (32 * st + m) * kKRow + 16 * hi;
 #pragma unroll
                 for (int ks = 0; ks < kQS; ++ks) {
-                    const h8 kv = *reinterpret_cast<const h8*>(kb + 32 * ks);
 #pragma unroll
                     for (int nt = 0; nt < kNT; ++nt)
-                        sacc[nt][st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qv[nt][ks], sacc[nt][st], 0, 0, 0);
+                        sacc[nt][st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[st][ks], qv[nt][ks], sacc[nt][st], 0, 0, 0);
                 }
             }
+            h8 vop[kDT][2 * kSub];
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+                for (int ks = 0; ks < 2 * kSub; ++ks)
+                    vop[dt][ks] = *reinterpret_cast<const h8*>(vt + (32 * dt + m) * kVRow + 16 * hi + 32 * ks);
+            __builtin_amdgcn_sched_barrier(0);
             const bool need_mask = k0 + KT - 1 > w_pos_lo;
             h8 pb[kNT][2 * kSub];
 #pragma unroll
@@ -343,13 +358,11 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
             // O^T += V^T P^T: each V operand feeds kNT products.
 #pragma unroll
             for (int dt = 0; dt < kDT; ++dt) {
-                const unsigned char* vb = vt + (32 * dt + m) * kVRow + 16 * hi;
 #pragma unroll
                 for (int ks = 0; ks < 2 * kSub; ++ks) {
-                    const h8 vv = *reinterpret_cast<const h8*>(vb + 32 * ks);
 #pragma unroll
                     for (int nt = 0; nt < kNT; ++nt)
-                        acc_o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pb[nt][ks], acc_o[nt][dt], 0, 0, 0);
+                        acc_o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[dt][ks], pb[nt][ks], acc_o[nt][dt], 0, 0, 0);
                 }
             }
         }
