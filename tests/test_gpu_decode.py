@@ -259,3 +259,27 @@ def test_decode_full_size_sampled(name, seqs):
     kc, vc = oracle_caches(p)
     ref = oracle_out(p, kc, vc, seqs)
     check_close(out[seqs], ref, name)
+
+
+LARGE_BATCH = W.shrink(W.MIX, name="large_batch", num_seqs=150, num_blocks=4096, max_blocks_per_seq=32,
+                       num_q_heads=16, num_kv_heads=4)
+
+
+def large_batch_lens():
+    rng = np.random.default_rng(17)
+    lens = [int(x) for x in rng.integers(1, 400, size=LARGE_BATCH.num_seqs)]
+    lens[5] = lens[77] = 1               # single-token contexts
+    lens[140] = 400                      # a table row filled to the last block
+    return lens
+
+
+@pytest.mark.parametrize("N", [0, 7, 333])
+def test_decode_batch_larger_than_a_wave(N):
+    """More than 64 sequences: context lengths no longer fit one wave's
+    registers, so the split kernel and the merge kernel scan them from memory.
+    Every row is checked against the oracle."""
+    lens = large_batch_lens()
+    p = build(LARGE_BATCH, lambda a: W._plain_plan(a, LARGE_BATCH, lens))
+    out = run_step(p, num_splits=N)
+    kc, vc = oracle_caches(p)
+    check_close(out, oracle_out(p, kc, vc), f"large batch N={N}")

@@ -190,3 +190,15 @@ def test_prefill_cache_larger_than_4gib():
     check_close(out, ref, "prefill > 4 GiB pool")
     del kc, vc
     torch.cuda.empty_cache()
+
+
+def test_prefill_many_short_chunks():
+    """100 sequences with chunks of 1..40 rows over contexts of up to 200
+    tokens, grouped heads."""
+    rng = np.random.default_rng(23)
+    lens = [int(x) for x in rng.integers(1, 200, size=100)]
+    chunks = [int(min(L, x)) for L, x in zip(lens, rng.integers(1, 41, size=100))]
+    chunks[3] = 0
+    p = make(8, 2, 128, 16, lens, chunks, seed=23)
+    out = run(p, 0.0883883)
+    check_close(out, oracle(p, 0.0883883), "prefill many short chunks")
