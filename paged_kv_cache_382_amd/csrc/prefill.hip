@@ -59,8 +59,14 @@ __device__ __forceinline__ int v_slot(int k) {
     return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-__device__ __forceinline__ float xor32(float x) {
-    return __shfl_xor(x, 32, 64);
+// The two halves of a wave hold different keys of the same query rows (lane l
+// and lane l ^ 32 share row l % 32): every lane receives both halves' values
+// of its row, swapped across the halves by v_permlane32_swap.
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+    b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
 }
 
 // XCD-aware order: consecutive work items (the row tiles of one sequence and
@@ -287,18 +293,18 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
                     kop[st][ks] = *reinterpret_cast<const h8*>(kt + (32 * st + m) * kKRow + 16 * hi + 32 * ks);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int st = 0; st < kSub; ++st) {
+            for (int st = 0; st < kSub; ++st)
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sacc[nt][st][r] = 0.0f;
 #pragma unroll
-                for (int ks = 0; ks < kQS; ++ks) {
+            for (int ks = 0; ks < kQS; ++ks)
+#pragma unroll
+                for (int st = 0; st < kSub; ++st)
 #pragma unroll
                     for (int nt = 0; nt < kNT; ++nt)
                         sacc[nt][st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[st][ks], qv[nt][ks], sacc[nt][st], 0, 0, 0);
-                }
-            }
             h8 vop[kDT][2 * kSub];
 #pragma unroll
             for (int dt = 0; dt < kDT; ++dt)
@@ -319,12 +325,20 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
                             if (key > row_pos[nt]) sacc[nt][st][r] = kNegBig;
                         }
                 }
-                float mx = kNegBig;
+                float mv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) mv[i] = kNegBig;
 #pragma unroll
                 for (int st = 0; st < kSub; ++st)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nt][st][r]);
-                mx = fmaxf(mx, xor32(mx)) * c_log2;
+                    for (int r = 0; r < 16; ++r) mv[r & 7] = fmaxf(mv[r & 7], sacc[nt][st][r]);
+                float mx = fmaxf(fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])),
+                                 fmaxf(fmaxf(mv[4], mv[5]), fmaxf(mv[6], mv[7])));
+                {
+                    float ma, mb;
+                    halves(mx, ma, mb);
+                    mx = fmaxf(ma, mb) * c_log2;
+                }
                 const bool grow = mx > m_ref[nt] + kSlack;
                 if (__ballot(grow)) {
                     const float m_new = grow ? mx : m_ref[nt];
@@ -357,14 +371,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
                     }
             // O^T += V^T P^T: each V operand feeds kNT products.
 #pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) {
+            for (int ks = 0; ks < 2 * kSub; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < 2 * kSub; ++ks) {
+                for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
                     for (int nt = 0; nt < kNT; ++nt)
                         acc_o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[dt][ks], pb[nt][ks], acc_o[nt][dt], 0, 0, 0);
-                }
-            }
         }
         // Stage tile t+1 into the other buffer (last read before the previous
         // barrier), put tile t+2 in flight, fetch the ids of tile t+3.
@@ -380,7 +392,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-        const float l_tot = l_sum[nt] + xor32(l_sum[nt]);
+        float la, lb;
+        halves(l_sum[nt], la, lb);
+        const float l_tot = la + lb;
         if (!row_ok[nt]) continue;
         const float inv = 1.0f / l_tot;
         _Float16* op = reinterpret_cast<_Float16*>(a.out) +
