@@ -51,3 +51,24 @@ def test_table_overhead_below_one_percent():
 def test_store_and_copy_bytes():
     assert bench.store_bytes(32, 32, 128) == 4 * 32 * 32 * 128 * 2 + 128
     assert bench.copy_bytes(1, 16, 8, 128) == 4 * 16 * 8 * 128 * 2
+
+
+@pytest.mark.parametrize("lens,chunks", [([7], [7]), ([10, 3, 5], [4, 3, 0]), ([2048] * 2, [256] * 2)])
+def test_prefill_flops_brute_force(lens, chunks):
+    """Causal key counts by enumeration: row j of an n-row chunk at the end of
+    an L-token context sees L - n + j + 1 keys; 4 flops a key, dim and head."""
+    hq, d = 3, 8
+    keys = sum(L - n + j + 1 for L, n in zip(lens, chunks) for j in range(n))
+    assert bench.prefill_flops(lens, chunks, hq, d) == 4 * keys * hq * d
+
+
+def test_prefill_flops_benchmarked_workload():
+    # 32 chunks of 256 rows ending 2048-token prompts, 32 query heads, D = 128:
+    # each chunk sees 256*1792 + 256*257/2 = 491,648 keys
+    assert bench.prefill_flops([2048] * 32, [256] * 32, 32, 128) == 4 * 491_648 * 32 * 128 * 32
+    assert bench.prefill_flops([2048] * 32, [256] * 32, 32, 128) == 257_765_146_624
+
+
+def test_prefill_kv_bytes():
+    # K and V rows of every context token once: 2048 tokens x 8 heads x 128 x 2 B x 2
+    assert bench.prefill_kv_bytes([2048], 8, 128) == 2048 * 8 * 128 * 4
