@@ -13,7 +13,8 @@ its own K/V cache so that the 256 MB last-level cache cannot serve re-reads.
 Prints one JSON line.  ``value`` is the step's algorithmic HBM traffic divided
 by its time (GB/s); ``roofline`` reports the decode call alone, timed with
 HIP events around each call inside the timed region; ``cpu_baseline`` is the
-fp64 CPU oracle on a bounded sample of the same workload.
+fp64 CPU oracle on a bounded sample of the same workload; ``graph`` times the
+same step replayed as one captured HIP graph (``--no-graph`` skips it).
 
     python bench.py [--steps K] [--warmup W] [--workload mha|mix|prefix|long_bs16|...]
 
@@ -412,8 +413,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured as one HIP graph (reported under 'graph')")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip timing the step captured as one HIP graph (reported under 'graph')")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over half the pool of one layer (a plain copy "
                          "of known size, for scaling the HBM byte counters) and exit")
