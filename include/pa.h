@@ -222,7 +222,7 @@ int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads,
  *                  are not written
  *   scale          positive and finite
  *
- * head_dim 64 or 128; any block_size; any group size.  Lengths are clamped
+ * head_dim 64 or 128; block_size a power of two; any group size.  Lengths are clamped
  * on the device so that nothing outside the buffers is read; an out-of-range
  * table entry reads as zero rows (the result of rows that see it is then
  * unspecified).  PA_VALIDATE checks all of this on the host first.  No

@@ -148,3 +148,8 @@ def test_prefill_rejects_bad_arguments(kw, desc, code):
 def test_prefill_empty_batch_is_a_no_op():
     assert call_prefill(B=0, q=None, out=None) == 0
     assert call_prefill(T=0, q=None, out=None) == 0
+
+
+def test_prefill_rejects_block_sizes_that_are_not_powers_of_two():
+    assert call_prefill(_desc(bs=12)) == NAMES["UNSUPPORTED"]
+    assert call_prefill(_desc(bs=24)) == NAMES["UNSUPPORTED"]
