@@ -283,3 +283,35 @@ def test_decode_batch_larger_than_a_wave(N):
     out = run_step(p, num_splits=N)
     kc, vc = oracle_caches(p)
     check_close(out, oracle_out(p, kc, vc), f"large batch N={N}")
+
+
+def random_configs(n=12, seed=31):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2, 4]))
+        bs = int(rng.choice([8, 16, 32, 64]))
+        b = int(rng.integers(1, 20))
+        lens = [int(x) for x in rng.integers(1, 700, size=b)]
+        if b > 2:
+            lens[int(rng.integers(b))] = 1
+        n_split = int(rng.choice([0, 0, 1, 3, 64, 999]))
+        out.append((i, d, g, hkv, bs, lens, n_split))
+    return out
+
+
+@pytest.mark.parametrize("cfg", random_configs(), ids=lambda c: f"r{c[0]}_d{c[1]}_g{c[2]}_bs{c[4]}")
+def test_decode_random_configurations(cfg):
+    """Seeded random shapes: head dim, group, KV heads, block size, batch,
+    ragged lengths (with single-token contexts) and split counts."""
+    i, d, g, hkv, bs, lens, n_split = cfg
+    m = max(-(-L // bs) for L in lens)
+    nb = sum(-(-L // bs) for L in lens) + 16
+    wl = W.shrink(W.MIX, name=f"random{i}", num_seqs=len(lens), num_q_heads=g * hkv, num_kv_heads=hkv,
+                  head_dim=d, block_size=bs, num_blocks=nb, max_blocks_per_seq=m, seed=100 + i)
+    p = build(wl, lambda a: W._plain_plan(a, wl, lens))
+    out = run_step(p, num_splits=n_split)
+    kc, vc = oracle_caches(p)
+    check_close(out, oracle_out(p, kc, vc), f"random config {i}")

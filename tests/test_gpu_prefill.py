@@ -202,3 +202,22 @@ def test_prefill_many_short_chunks():
     p = make(8, 2, 128, 16, lens, chunks, seed=23)
     out = run(p, 0.0883883)
     check_close(out, oracle(p, 0.0883883), "prefill many short chunks")
+
+
+def test_prefill_long_context_sampled():
+    """Two 32768-token contexts with 256-row chunks (block ids past the first
+    thousand table entries), sampled rows against single-query attention over
+    each row's prefix."""
+    lens, chunks = [32768, 30001], [256, 256]
+    p = make(8, 2, 128, 16, lens, chunks, seed=41)
+    out = run(p, 0.0883883)
+    h = p["host"]
+    got, ref = [], []
+    for s in range(2):
+        for j in [0, 77, 255]:
+            t = int(h["starts"][s]) + j
+            pos = int(h["lens"][s]) - 256 + j
+            r = decode_ref(h["q"][t:t + 1], h["k"], h["v"], h["tables"][s:s + 1], [pos + 1], 0.0883883)
+            got.append(out[t])
+            ref.append(r[0])
+    check_close(torch.stack(got), np.stack(ref), "prefill long context")
