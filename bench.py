@@ -121,7 +121,8 @@ def counter_traffic(wl_name, kind="decode"):
     """HBM bytes per launch of the ``kind`` kernel from committed rocprofv3
     counter runs, or None when that kernel's source changed since they were
     taken."""
-    path = os.path.join(ROOT, "profiles", f"{kind}_{wl_name}_counters.json")
+    stem = wl_name if wl_name.startswith(kind + "_") else f"{kind}_{wl_name}"
+    path = os.path.join(ROOT, "profiles", f"{stem}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -130,6 +131,12 @@ def counter_traffic(wl_name, kind="decode"):
     if rec.get(f"{kind}_source_sha256_16") != source_digest(src):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def pcts(xs):
+    """p10 / median / p90 of a list of timings."""
+    return {"p10": round(float(np.percentile(xs, 10)), 4), "median": round(float(np.median(xs)), 4),
+            "p90": round(float(np.percentile(xs, 90)), 4)}
 
 
 def host_step_cost(wl, reps=20):
@@ -159,9 +166,27 @@ def host_step_cost(wl, reps=20):
             "reps": len(lat)}
 
 
-def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s):
+# The numerics bar of the decode output against the fp64 oracle (the tests
+# assert it; here it is reported beside the measured errors).
+PARITY_BAR = {"max_abs": 4e-3, "mean_abs": 5e-4, "rel_l2": 1e-3}
+
+
+def parity_summary(diffs, refs):
+    """max-abs, mean-abs and relative L2 of the GPU rows against the oracle's."""
+    d = np.concatenate([x.ravel() for x in diffs])
+    r = np.concatenate([x.ravel() for x in refs])
+    out = {"max_abs": float(np.abs(d).max()), "mean_abs": float(np.abs(d).mean()),
+           "rel_l2": float(np.linalg.norm(d) / max(np.linalg.norm(r), 1e-30))}
+    out["within_bar"] = all(out[k] <= PARITY_BAR[k] for k in PARITY_BAR)
+    out["bar"] = PARITY_BAR
+    return out
+
+
+def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None):
     """The fp64 oracle on the host cores: one layer, sequences taken in batch
-    order until about ``budget_s`` seconds of work."""
+    order until about ``budget_s`` seconds of work.  With ``out0`` (the GPU's
+    output of the same layer) the first pass over the batch is also compared
+    with it, row by row, and reported under ``parity``."""
     from threadpoolctl import threadpool_limits
 
     from oracle import decode_ref
@@ -170,6 +195,8 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s):
     kh = kc0.cpu().numpy()
     vh = vc0.cpu().numpy()
     qh = q0.cpu().numpy()
+    gpu = out0.float().cpu().numpy().astype(np.float64) if out0 is not None else None
+    diffs, refs = [], []
     tables = np.asarray(plan.block_tables, dtype=np.int32)
     lens = np.asarray(plan.context_lens, dtype=np.int32)
     done, tokens, nbytes, elapsed = 0, 0, 0, 0.0
@@ -177,13 +204,16 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s):
         while elapsed < budget_s and done < 64 * len(lens):
             s = done % len(lens)
             t0 = time.perf_counter()
-            decode_ref(qh[s:s + 1], kh, vh, tables[s:s + 1], lens[s:s + 1], wl.scale)
+            ref = decode_ref(qh[s:s + 1], kh, vh, tables[s:s + 1], lens[s:s + 1], wl.scale)
             elapsed += time.perf_counter() - t0
+            if gpu is not None and done < len(lens):
+                diffs.append(gpu[s] - ref[0])
+                refs.append(ref[0])
             done += 1
             tokens += int(lens[s])
             nbytes += decode_bytes(lens[s:s + 1], wl.num_q_heads, wl.num_kv_heads,
                                    wl.head_dim, wl.block_size)
-    return {
+    result = {
         "value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, one layer of the same workload: {done} sequence "
@@ -191,6 +221,37 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s):
                    f"{elapsed:.2f} s"),
         "tokens_per_s_extrapolated": round(done / (elapsed * wl.layers), 4),
     }
+    if diffs:
+        result["parity"] = dict(parity_summary(diffs, refs), sequences=len(diffs),
+                                compared="layer 0 output of the timed steps, fp16, against the oracle")
+    return result
+
+
+def read_ceiling(buffers, reps):
+    """The streaming-read rate of the device on the given resident buffers:
+    ``pa_read_probe`` over each, ``reps`` times, timed with HIP events; the
+    median launch is reported."""
+    import torch
+
+    import paged_kv_cache_382_amd as pa
+    sink = torch.zeros(1, dtype=torch.int32, device=buffers[0].device)
+    for b in buffers:
+        pa.pa_read_probe(b, sink)
+    torch.cuda.synchronize()
+    times, nbytes = [], []
+    for _ in range(reps):
+        for b in buffers:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pa.pa_read_probe(b, sink)
+            e1.record()
+            times.append((e0, e1))
+            nbytes.append(b.numel() * b.element_size())
+    torch.cuda.synchronize()
+    rates = [n / (a.elapsed_time(b) * 1e-3) / 1e9 for n, (a, b) in zip(nbytes, times)]
+    return {"gbps": round(float(np.median(rates)), 2), "bytes_per_launch": int(nbytes[0]),
+            "launches": len(rates), "kernel": "read_probe_kernel (pa_read_probe: 16-byte "
+            "non-temporal loads, one contiguous range per workgroup)"}
 
 
 def copy_probe(wl, dev, reps):
@@ -268,10 +329,12 @@ def compaction_probe(wl, dev, reps):
         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}), flush=True)
 
 
-def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s):
+def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s, out0=None):
     """The oracle timed on the host: causal rows of the first sequence's
     chunk, each row being single-query attention over its prefix (the
-    reduction the prefill oracle is pinned to), until ``budget_s`` passes."""
+    reduction the prefill oracle is pinned to), until ``budget_s`` passes.
+    With ``out0`` (the GPU's output rows of the same layer) every computed row
+    is also compared with it and reported under ``parity``."""
     import torch
 
     from oracle import prefill_ref
@@ -284,20 +347,29 @@ def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s):
     v_host = vc[torch.from_numpy(row).to(vc.device)].cpu().numpy()
     q_host = q[:chunk].cpu().numpy()
     local = np.arange(nb, dtype=np.int32)[None, :]
+    gpu = out0[:chunk].float().cpu().numpy().astype(np.float64) if out0 is not None else None
+    diffs, refs = [], []
     done, flops, t0 = 0, 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s and done < chunk:
         j = done
         pos = L - chunk + j
-        prefill_ref(q_host[j:j + 1], k_host, v_host, local, [pos + 1], [0, 1], wl.scale)
+        ref = prefill_ref(q_host[j:j + 1], k_host, v_host, local, [pos + 1], [0, 1], wl.scale)
         flops += 4 * (pos + 1) * wl.num_q_heads * wl.head_dim
+        if gpu is not None:
+            diffs.append(gpu[j] - ref[0])
+            refs.append(ref[0])
         done += 1
     elapsed = time.perf_counter() - t0
-    return {
+    result = {
         "value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle: {done} causal rows (all {wl.num_q_heads} query heads) "
                    f"of one sequence's chunk, one layer, in {elapsed:.2f} s"),
     }
+    if diffs:
+        result["parity"] = dict(parity_summary(diffs, refs), rows=len(diffs),
+                                compared="layer 0 output rows of the timed steps, fp16, against the oracle")
+    return result
 
 
 def prefill_main(args, wl, dev):
@@ -351,14 +423,16 @@ def prefill_main(args, wl, dev):
     torch.cuda.synchronize()
     events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
                for _ in range(layers)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
     for k in range(args.steps):
         step(events[k])
-    end.record()
+        marks[k + 1].record()
     torch.cuda.synchronize()
-    step_ms = start.elapsed_time(end) / args.steps
-    pf_ms = float(np.mean([e[0].elapsed_time(e[1]) for row in events for e in row]))
+    step_ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_each = [marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)]
+    pf_each = [e[0].elapsed_time(e[1]) for row in events for e in row]
+    pf_ms = float(np.mean(pf_each))
     lens = [int(x) for x in lens_h]
     flops = prefill_flops(lens, [chunk] * B, hq, d)
     value = layers * flops / (step_ms * 1e-3) / 1e12
@@ -384,6 +458,8 @@ def prefill_main(args, wl, dev):
         },
         "prefill_tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "prefill_us_per_layer": round(pf_ms * 1e3, 3),
+        "step_ms_percentiles": pcts(step_each),
+        "prefill_us_percentiles": pcts([x * 1e3 for x in pf_each]),
         "roofline": {
             "bound": "mfma",
             "kernel": "pa_prefill (prefill_kernel)",
@@ -398,7 +474,8 @@ def prefill_main(args, wl, dev):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = prefill_cpu_baseline(wl, caches[0][0], caches[0][1], q[0],
-                                                      tables_h, lens_h, chunk, args.cpu_budget)
+                                                      tables_h, lens_h, chunk, args.cpu_budget,
+                                                      out0=out[0])
     print(json.dumps(result), flush=True)
 
 
@@ -413,6 +490,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read probe on layer 0's caches")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip timing the step captured as one HIP graph (reported under 'graph')")
     ap.add_argument("--copy-probe", action="store_true",
@@ -496,14 +575,15 @@ def main():
     torch.cuda.synchronize()
     events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
                for _ in range(layers)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
+    marks[0].record()
     for k in range(args.steps):
         step(events[k])
-    end.record()
+        marks[k + 1].record()
     torch.cuda.synchronize()
-    step_ms = start.elapsed_time(end) / args.steps
+    step_ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_each = [marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)]
     dec_ms = [e[0].elapsed_time(e[1]) for row in events for e in row]
     dec_avg_ms = float(np.mean(dec_ms))
 
@@ -521,6 +601,8 @@ def main():
         ge.record()
         torch.cuda.synchronize()
         graph = gs.elapsed_time(ge) / args.steps
+
+    ceiling = None if args.no_read_ceiling else read_ceiling(list(caches[0]), 5)
 
     n_dec = decode_bytes(lens, hq, hkv, d, bs)
     n_step = layers * (n_dec + store_bytes(B, hkv, d) + copy_bytes(len(plan.cow_pairs), bs, hkv, d))
@@ -550,6 +632,8 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "decode_tokens_per_s": round(B / (step_ms * 1e-3), 2),
         "decode_us_per_layer": round(dec_avg_ms * 1e3, 3),
+        "step_ms_percentiles": pcts(step_each),
+        "decode_us_percentiles": pcts([x * 1e3 for x in dec_ms]),
         "roofline": {
             "bound": "hbm",
             "kernel": "pa_decode (balanced split kernel + merge kernel)",
@@ -567,13 +651,16 @@ def main():
                       "cow_pairs_this_step": len(plan.cow_pairs)},
         "host_step_us": host_step_cost(wl),
     }
+    if ceiling is not None:
+        result["read_ceiling"] = ceiling
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
     if graph is not None:
         result["graph"] = {"ms_per_step": round(graph, 4),
                            "value": round(n_step / (graph * 1e-3) / 1e9, 2),
                            "decode_tokens_per_s": round(B / (graph * 1e-3), 2)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, plan, caches[0][0], caches[0][1], q[0],
-                                              args.cpu_budget)
+                                              args.cpu_budget, out0=out[0])
     print(json.dumps(result, default=lambda o: o.item() if hasattr(o, "item") else str(o)),
           flush=True)
 

@@ -194,6 +194,24 @@ int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads,
                              int32_t num_splits);
 
 /* ----------------------------------------------------------------------- */
+/* Streaming-read probe: a measurement helper, not a step of the attention
+ * path.  [vLLM-core] section 3 ("Continuous batching") ties decode speed to
+ * memory bandwidth; this call reads a buffer once at the rate the device
+ * streams plain reads, so that the decode kernel's bandwidth can be set
+ * beside it in the same run on the same memory.
+ *
+ *   buf     device, 16-byte aligned, `bytes` readable bytes; read once with
+ *           16-byte non-temporal loads spread over the whole device
+ *   bytes   a multiple of 16; 0 launches nothing
+ *   sink    device uint32, 4-byte aligned: written (with 0x9E3779B9) only if
+ *           the XOR of the 32-bit words one lane read equals 0x9E3779B9, so
+ *           the loads cannot be optimised away; normally left untouched
+ *
+ * Enqueued on hip_stream; returns after the launch.  Errors: PA_ERR_SHAPE
+ * (bytes not a multiple of 16), PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_HIP. */
+pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream);
+
+/* ----------------------------------------------------------------------- */
 /* Chunked prefill: causal attention of packed prompt chunks over the cache.
  *
  * Sources: [PA-mem] "Deployable configuration parameters" (prompts are

@@ -37,6 +37,7 @@ SOURCES = [
     ("store_kvcache.hip", "hip"),
     ("decode.hip", "hip"),
     ("prefill.hip", "hip"),
+    ("probe.hip", "hip"),
 ]
 
 

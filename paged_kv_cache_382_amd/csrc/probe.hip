@@ -1,0 +1,56 @@
+// Streaming-read probe: a measurement helper, not a step of the attention path.
+//
+// The pages tie decode speed to memory bandwidth ("vLLM core architecture
+// ...", section 3, "Continuous batching").  This kernel reads a device buffer
+// once, as fast as the device streams reads, so that the decode kernel's
+// bandwidth can be set beside what the same device reaches with nothing but
+// reads, on the same buffer, in the same run.
+//
+// Design: the buffer is cut into equal contiguous ranges, one per workgroup
+// (at most 4096 of them, 256 lanes each); every lane keeps 16 non-temporal
+// 16-byte loads in flight.  The words are folded with XOR and the result is
+// stored only when it equals a fixed constant, so the loads cannot be dropped
+// and nothing is written in practice.
+
+#include "kernels.h"
+
+namespace pa {
+namespace {
+
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+constexpr int kProbeLanes = 256;
+constexpr int kProbeUnroll = 16;
+constexpr int64_t kProbeMaxGroups = 4096;
+
+__global__ __launch_bounds__(kProbeLanes) void read_probe_kernel(const u4* __restrict__ p, int64_t n_vec,
+                                                                 int64_t per_group, uint32_t* sink) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * per_group;
+    const int64_t end = begin + per_group < n_vec ? begin + per_group : n_vec;
+    unsigned acc = 0;
+    for (int64_t i = begin + threadIdx.x; i < end; i += kProbeLanes * kProbeUnroll) {
+        u4 v[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) {
+            const int64_t j = i + static_cast<int64_t>(u) * kProbeLanes;
+            v[u] = j < end ? __builtin_nontemporal_load(p + j) : u4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    if (acc == kReadProbeMagic) *sink = acc;
+}
+
+}  // namespace
+
+hipError_t launch_read_probe(const void* buf, int64_t n_vec16, uint32_t* sink, hipStream_t stream) {
+    if (n_vec16 <= 0) return hipSuccess;
+    constexpr int64_t kPerIter = static_cast<int64_t>(kProbeLanes) * kProbeUnroll;
+    int64_t groups = (n_vec16 + kPerIter - 1) / kPerIter;
+    groups = groups < kProbeMaxGroups ? groups : kProbeMaxGroups;
+    const int64_t per_group = (n_vec16 + groups - 1) / groups;
+    hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(groups)), dim3(kProbeLanes), 0, stream,
+                       static_cast<const u4*>(buf), n_vec16, per_group, sink);
+    return hipGetLastError();
+}
+
+}  // namespace pa

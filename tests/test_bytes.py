@@ -72,3 +72,18 @@ def test_prefill_flops_benchmarked_workload():
 def test_prefill_kv_bytes():
     # K and V rows of every context token once: 2048 tokens x 8 heads x 128 x 2 B x 2
     assert bench.prefill_kv_bytes([2048], 8, 128) == 2048 * 8 * 128 * 4
+
+
+@pytest.mark.parametrize("name", sorted(f for f in os.listdir(os.path.join(os.path.dirname(bench.__file__), "profiles"))
+                                        if f.endswith("_counters.json")))
+def test_committed_counter_runs_reach_the_bench_line(name):
+    """Every committed counter summary whose kernel source is unchanged is the
+    traffic bench.py reports for its workload."""
+    kind, wl = name[:-len("_counters.json")].split("_", 1)
+    src = bench.DECODE_SRC if kind == "decode" else bench.PREFILL_SRC
+    with open(os.path.join(os.path.dirname(bench.__file__), "profiles", name)) as f:
+        rec = json.load(f)
+    if rec[f"{kind}_source_sha256_16"] != bench.source_digest(src):
+        pytest.skip(f"{kind} kernel changed since {name} was taken")
+    wl_name = f"{kind}_{wl}" if kind == "prefill" else wl
+    assert bench.counter_traffic(wl_name, kind) == rec["hbm_bytes_per_launch"]

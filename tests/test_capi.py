@@ -153,3 +153,19 @@ def test_prefill_empty_batch_is_a_no_op():
 def test_prefill_rejects_block_sizes_that_are_not_powers_of_two():
     assert call_prefill(_desc(bs=12)) == NAMES["UNSUPPORTED"]
     assert call_prefill(_desc(bs=24)) == NAMES["UNSUPPORTED"]
+
+
+@pytest.mark.parametrize("buf,nbytes,sink,code", [
+    (0x1000, 24, 0x2000, "SHAPE"),                 # not a multiple of 16
+    (None, 32, 0x2000, "NULL"),
+    (0x1000, 32, None, "NULL"),
+    (0x1008, 32, 0x2000, "ALIGN"),
+    (0x1000, 32, 0x2002, "ALIGN"),
+])
+def test_read_probe_rejects_bad_arguments(buf, nbytes, sink, code):
+    assert pa.lib().pa_read_probe(buf, nbytes, sink, None) == NAMES[code]
+    assert pa.lib().pa_last_error().decode()
+
+
+def test_read_probe_of_nothing_launches_nothing():
+    assert pa.lib().pa_read_probe(None, 0, None, None) == 0
