@@ -241,9 +241,10 @@ pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip
  *   scale          positive and finite
  *
  * head_dim 64 or 128; block_size a power of two; any group size.  Lengths are clamped
- * on the device so that nothing outside the buffers is read; an out-of-range
- * table entry reads as zero rows (the result of rows that see it is then
- * unspecified).  PA_VALIDATE checks all of this on the host first.  No
+ * on the device so that nothing outside the buffers is read; a key behind an
+ * out-of-range table entry takes its K row from slot 0 of the cache and a zero
+ * V row (the result of rows that see it is then unspecified).  PA_VALIDATE
+ * checks all of this on the host first.  No
  * workspace; enqueued on hip_stream.
  */
 pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,

@@ -35,8 +35,10 @@
 //     accumulators as the B operand: accumulator register r of a 32-key
 //     sub-tile holds key (r/4)*8 + 4*(l/32) + r%4, which is MFMA k-slot
 //     8*(l/32) + r%8 of k-step r/8 once V's keys are stored in slot order.
-// Keys past the context or behind an out-of-range table entry read a safe
-// address; their V rows are zeroed when staged and their scores are masked.
+// Keys past the context or behind an out-of-range table entry read slot 0 of
+// the cache (a safe address) and their V rows are zeroed when staged; keys
+// past the context are also behind every row's causal limit, so their scores
+// are masked.
 // The output is normalised once and rounded to fp16 (round to nearest even).
 
 #include "kernels.h"
