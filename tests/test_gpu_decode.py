@@ -11,7 +11,7 @@ import torch
 
 import paged_kv_cache_382_amd as pa
 import workloads as W
-from oracle import decode_ref
+from oracle import decode_ref, store_ref
 from tests.gpu_problems import (DEV, build, check_close, host_u16, oracle_caches, oracle_out,
                                 run_step, say)
 
@@ -315,3 +315,59 @@ def test_decode_random_configurations(cfg):
     out = run_step(p, num_splits=n_split)
     kc, vc = oracle_caches(p)
     check_close(out, oracle_out(p, kc, vc), f"random config {i}")
+
+
+def test_store_copy_decode_cache_larger_than_4gib():
+    """A pool whose caches exceed 4 GiB with the sequences' blocks at its top:
+    the store, a block copy between two top blocks and decode all address past
+    4 GiB.  The oracle runs on a compact host cache holding the same rows."""
+    hq, hkv, d, bs = 16, 4, 128, 16
+    block_bytes = bs * hkv * d * 2
+    nb = (1 << 32) // block_bytes + 256
+    lens = [300, 77, 1000]
+    m = 64
+    order = np.arange(nb - 1, -1, -1, dtype=np.int32)          # highest blocks first
+    alloc = pa.Allocator(nb, bs, m, order)
+    slots = []
+    for s, L in enumerate(lens):
+        slots += list(alloc.add_seq(s, L))
+    tables, lens_arr = alloc.export(list(range(len(lens))), m)
+    assert min(int(x) // bs for x in slots) * block_bytes >= 1 << 32
+    say(f"decode: caches of {nb * block_bytes / 2**30:.2f} GiB each")
+    kc = torch.empty((nb, bs, hkv, d), dtype=torch.float16, device=DEV)
+    vc = torch.empty_like(kc)
+    k_rows = W.normal_fp16((len(slots), hkv, d), 81, DEV)
+    v_rows = W.normal_fp16((len(slots), hkv, d), 82, DEV)
+    say("decode > 4 GiB: store")
+    pa.pa_store_kvcache(k_rows, v_rows, torch.tensor(slots, dtype=torch.int32, device=DEV), kc, vc)
+    # copy the first block of sequence 2 onto a free block near the top, and
+    # point sequence 2's table at the copy
+    src = int(tables[2][0])
+    dst = int(alloc.free_list()[0])
+    assert dst * block_bytes >= 1 << 32
+    say(f"decode > 4 GiB: copy block {src} -> {dst}")
+    pa.pa_copy_blocks(kc, vc, torch.tensor([[src, dst]], dtype=torch.int32, device=DEV))
+    tables = np.array(tables, dtype=np.int32)
+    tables[2][0] = dst
+    q = W.normal_fp16((len(lens), hq, d), 83, DEV)
+    say("decode > 4 GiB: decode")
+    out = pa.pa_decode(q, kc, vc, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens_arr).to(DEV),
+                       0.0883883, max_context_len=max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(kc[dst].view(torch.int16), kc[src].view(torch.int16))
+    assert torch.equal(vc[dst].view(torch.int16), vc[src].view(torch.int16))
+    # compact oracle cache: used block i of the tables becomes block i
+    used = sorted({int(b) for row, L in zip(tables, lens_arr) for b in row[:-(-int(L) // bs)]} | {src})
+    remap = {b: i for i, b in enumerate(used)}
+    small_tables = np.array([[remap.get(int(b), 0) for b in row] for row in tables], dtype=np.int32)
+    small_slots = [remap[s // bs] * bs + s % bs for s in slots]
+    shape = (len(used), bs, hkv, d)
+    kh, vh = store_ref(host_u16(k_rows).view(np.float16), host_u16(v_rows).view(np.float16), small_slots,
+                       np.zeros(shape, np.uint16), np.zeros(shape, np.uint16))
+    kh[remap[dst]] = kh[remap[src]]
+    vh[remap[dst]] = vh[remap[src]]
+    ref = decode_ref(host_u16(q).view(np.float16), kh.view(np.float16), vh.view(np.float16),
+                     small_tables, lens_arr, 0.0883883)
+    check_close(out, ref, "decode > 4 GiB pool")
+    del kc, vc
+    torch.cuda.empty_cache()
