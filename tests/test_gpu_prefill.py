@@ -221,3 +221,35 @@ def test_prefill_long_context_sampled():
             got.append(out[t])
             ref.append(r[0])
     check_close(torch.stack(got), np.stack(ref), "prefill long context")
+
+
+def random_prefill_configs(n=12, seed=47):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 3, 4, 8]))
+        hkv = int(rng.choice([1, 2, 4]))
+        bs = int(rng.choice([4, 8, 16, 32, 64, 128]))
+        b = int(rng.integers(1, 7))
+        lens = [int(x) for x in rng.integers(1, 500, size=b)]
+        chunks = [int(rng.integers(0, L + 1)) for L in lens]
+        if b > 1:
+            chunks[0] = lens[0]                        # a whole prompt
+        if b > 2:
+            chunks[1] = 1                              # a single new row
+        if b > 3:
+            chunks[2] = 0                              # no rows this step
+        out.append((i, d, g, hkv, bs, lens, chunks))
+    return out
+
+
+@pytest.mark.parametrize("cfg", random_prefill_configs(), ids=lambda c: f"r{c[0]}_d{c[1]}_g{c[2]}_bs{c[4]}")
+def test_prefill_random_configurations(cfg):
+    """Seeded random shapes: head dim, group (odd ones too), KV heads, block
+    size, batch, ragged contexts and chunks (whole prompts, single rows, empty)."""
+    i, d, g, hkv, bs, lens, chunks = cfg
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    p = make(g * hkv, hkv, d, bs, lens, chunks, seed=200 + i)
+    out = run(p, scale)
+    check_close(out, oracle(p, scale), f"prefill random config {i}")
