@@ -158,6 +158,10 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  *                  fp32 partials (running max, sum, weighted values) from
  *                  each, which a second kernel combines, in range order, into
  *                  the output (online-softmax merge).  Must be in [0, 2^20].
+ *                  With 0, at most 64 sequences and max_context_len <= 512,
+ *                  each workgroup instead takes one whole (sequence, KV head)
+ *                  pair and writes its rows directly: a single launch, no
+ *                  merge (short contexts, where launches dominate).
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
  *                  bytes (same cache, num_seqs, num_q_heads, num_splits, on
  *                  the same device), 256-byte aligned, for those partials.

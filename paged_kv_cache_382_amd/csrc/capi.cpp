@@ -73,6 +73,11 @@ int32_t resolve_splits(const pa_cache_desc* c, int32_t num_q_heads, int32_t requ
     return std::min<int32_t>(resident_workgroups(c, num_q_heads), kMaxSplits);
 }
 
+// Contexts of at most this many tokens (and at most 64 sequences) are decoded
+// one workgroup per (sequence, KV head) pair: every pair is short, so the
+// grid stays balanced, and no merge launch is needed.
+constexpr int64_t kWholePairMaxTokens = 512;
+
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -296,6 +301,11 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     a.max_tokens = static_cast<int32_t>(max_tokens64);
     a.num_splits = splits;
     a.scale_log2 = scale * pa::kLog2e;
+    a.whole_pairs = 0;
+    if (num_splits == 0 && num_seqs <= 64 && max_tokens64 <= pa::kWholePairMaxTokens) {
+        a.whole_pairs = 1;
+        a.num_splits = static_cast<int32_t>(pairs);
+    }
     hipError_t err = pa::launch_decode(a, stream);
     if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
     return ok();

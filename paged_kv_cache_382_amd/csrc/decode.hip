@@ -21,6 +21,10 @@
 //
 // Design (HBM-bound streaming; no matrix cores: G <= 8 query rows never fill
 // an MFMA tile):
+//  * Short contexts (a bound of at most 512 tokens, at most 64 sequences):
+//    workgroup w takes (sequence, KV head) pair w whole and writes its fp16
+//    rows; no merge kernel runs.  One launch instead of two where launch
+//    latency, not bandwidth, sets the time.
 //  * Balanced split.  The work is the list of 16-token chunks of every
 //    (sequence, KV head) pair, in sequence-major order; the grid is W
 //    workgroups (by default as many as the device holds at once) and
@@ -533,8 +537,26 @@ void decode_split_kernel(const DecodeArgs a) {
     };
 
     const int u = blockIdx.x;
-    const int64_t start = static_cast<int64_t>(u) * U / N;
-    const int64_t end = static_cast<int64_t>(u + 1) * U / N;
+    int64_t start, end;
+    if (a.whole_pairs) {
+        // Pair u = (s, g) whole: its chunks follow Hkv * (chunks of the earlier
+        // sequences) + g * (its own chunk count).  An empty context has no
+        // chunk; its zero rows are written here (no merge kernel runs).
+        const int s = u / Hkv;
+        const int g = u - s * Hkv;
+        const int L = __builtin_amdgcn_readlane(len_reg, s);
+        const int nch = chunks_of(L);
+        if (nch == 0) {
+            for (int o = threadIdx.x; o < G * D; o += kThreads)
+                a.out[(static_cast<size_t>(s) * a.num_q_heads + g * G) * D + o] = 0;
+            return;
+        }
+        start = (readlane64(incl_reg, s) - nch) * Hkv + static_cast<int64_t>(g) * nch;
+        end = start + nch;
+    } else {
+        start = static_cast<int64_t>(u) * U / N;
+        end = static_cast<int64_t>(u + 1) * U / N;
+    }
     if (start < end) process_split(u, start, end);
 }
 
@@ -676,7 +698,7 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_split_kernel<D, BS, G>), dim3(a.num_splits), dim3(kThreads), 0,
                        stream, a);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || a.whole_pairs) return err;
     hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.num_seqs * a.num_kv_heads), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();

@@ -28,6 +28,8 @@ struct DecodeArgs {
     int32_t max_tokens;            // clamp of context lengths
     int32_t num_splits;            // N: equal pieces of the chunk list, one workgroup each
     float scale_log2;              // scale * log2(e)
+    int32_t whole_pairs;           // 1: workgroup w takes (sequence, KV head) pair w whole
+                                   // (N = num_seqs * num_kv_heads, at most 64 sequences, no merge)
 };
 
 bool decode_supported(int head_dim, int block_size, int group);

@@ -371,3 +371,46 @@ def test_store_copy_decode_cache_larger_than_4gib():
     check_close(out, ref, "decode > 4 GiB pool")
     del kc, vc
     torch.cuda.empty_cache()
+
+
+SHORT_LENS = [1, 16, 17, 200, 512, 33, 64, 300]
+
+
+def test_whole_pairs_short_contexts_with_empty_ones():
+    """Contexts of at most 512 tokens and the default split: one workgroup per
+    (sequence, KV head) pair and no merge launch.  Empty contexts still get
+    zero rows and every other row is written (the output starts as NaN)."""
+    p = build(MEDIUM, plan_fn=medium_plan(lens=SHORT_LENS))
+    out0 = run_step(p)                  # caches now hold the step's tokens
+    kc, vc = oracle_caches(p)
+    check_close(out0, oracle_out(p, kc, vc), "whole pairs")
+    lens = p["lens"].clone()
+    lens[1] = 0
+    lens[6] = 0
+    out = torch.full_like(p["q"], float("nan"))
+    say("whole pairs with empty contexts")
+    pa.pa_decode(p["q"], p["kc"], p["vc"], p["tables"], lens, MEDIUM.scale, out=out,
+                 max_context_len=p["max_ctx"])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[1]).item() == 0 and torch.count_nonzero(out[6]).item() == 0
+    r = p["ref"]
+    ref = decode_ref(r["q"], kc.view(np.float16), vc.view(np.float16), r["tables"],
+                     lens.cpu().numpy(), MEDIUM.scale)
+    keep = [0, 2, 3, 4, 5, 7]
+    check_close(out[keep], ref[keep], "whole pairs, empty contexts")
+
+
+def test_whole_pairs_agree_with_split_path_and_repeat_bitwise():
+    p = build(MEDIUM, plan_fn=medium_plan(lens=SHORT_LENS))
+    run_step(p)
+    args = (p["q"], p["kc"], p["vc"], p["tables"], p["lens"], MEDIUM.scale)
+    say("whole pairs twice, then 7 explicit splits")
+    a = pa.pa_decode(*args, max_context_len=p["max_ctx"])
+    b = pa.pa_decode(*args, max_context_len=p["max_ctx"])
+    c = pa.pa_decode(*args, max_context_len=p["max_ctx"], num_splits=7)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    kc, vc = oracle_caches(p)
+    ref = oracle_out(p, kc, vc)
+    check_close(a, ref, "whole pairs")
+    check_close(c, ref, "split path")
