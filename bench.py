@@ -220,6 +220,7 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None):
                    f"decodes ({tokens} context tokens, batch order, repeating) in "
                    f"{elapsed:.2f} s"),
         "tokens_per_s_extrapolated": round(done / (elapsed * wl.layers), 4),
+        "seconds_per_layer_extrapolated": round(elapsed / done * len(lens), 4),
     }
     if diffs:
         result["parity"] = dict(parity_summary(diffs, refs), sequences=len(diffs),
@@ -651,6 +652,8 @@ def main():
                       "cow_pairs_this_step": len(plan.cow_pairs)},
         "host_step_us": host_step_cost(wl),
     }
+    if traffic is not None:
+        result["roofline"]["traffic_over_algorithmic"] = round(traffic / n_dec, 4)
     if ceiling is not None:
         result["read_ceiling"] = ceiling
         result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
