@@ -55,7 +55,10 @@ typedef enum pa_status {
     PA_ERR_SEQ_LIMIT = 8,      /* allocator: max_blocks_per_seq reached       */
     PA_ERR_UNKNOWN_SEQ = 9,    /* allocator: no such sequence                 */
     PA_ERR_SEQ_EXISTS = 10,    /* allocator: sequence id already in use       */
-    PA_ERR_HIP = 11            /* a HIP runtime call failed                   */
+    PA_ERR_HIP = 11,           /* a HIP runtime call failed                   */
+    PA_ERR_HOST = 12           /* host memory ran out (or another host-side
+                                  failure); an allocator that returns it may
+                                  be partly updated and must be destroyed    */
 } pa_status;
 
 typedef struct pa_cache_desc {
@@ -273,7 +276,9 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
  * the back in logical order); initial_free_order, if not NULL, is a
  * permutation of [0, num_blocks) giving its first order, else 0..n-1.
  * Every operation either succeeds completely or fails with the state
- * unchanged.  Host memory only; one allocator must not be used by two threads
+ * unchanged, except PA_ERR_HOST (host memory exhausted mid-operation): the
+ * allocator must then be destroyed.  Host memory only; one allocator must not
+ * be used by two threads
  * at once.  Sequence ids are arbitrary int64 values.
  */
 typedef struct pa_allocator pa_allocator;

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libp
 STATUS = {
     0: "OK", 1: "NULL", 2: "SHAPE", 3: "ALIGN", 4: "UNSUPPORTED", 5: "RANGE",
     6: "WORKSPACE", 7: "OUT_OF_BLOCKS", 8: "SEQ_LIMIT", 9: "UNKNOWN_SEQ",
-    10: "SEQ_EXISTS", 11: "HIP",
+    10: "SEQ_EXISTS", 11: "HIP", 12: "HOST",
 }
 
 

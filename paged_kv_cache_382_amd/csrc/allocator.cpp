@@ -126,66 +126,72 @@ extern "C" {
 pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
                           int32_t max_blocks_per_seq,
                           const int32_t* initial_free_order, pa_allocator** out) {
-    if (!out) return fail(PA_ERR_NULL, "pa_alloc_create: out is NULL");
-    *out = nullptr;
-    if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
-        return fail(PA_ERR_SHAPE, "pa_alloc_create: sizes must be positive");
-    if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
-        return fail(PA_ERR_RANGE, "pa_alloc_create: num_blocks*block_size overflows int32 slots");
-    pa_allocator* a = new (std::nothrow) pa_allocator(num_blocks, block_size, max_blocks_per_seq);
-    if (!a) return fail(PA_ERR_RANGE, "pa_alloc_create: out of host memory");
-    if (initial_free_order) {
-        std::vector<char> seen(static_cast<size_t>(num_blocks), 0);
-        for (int32_t i = 0; i < num_blocks; ++i) {
-            int32_t b = initial_free_order[i];
-            if (b < 0 || b >= num_blocks || seen[b]) {
-                delete a;
-                return fail(PA_ERR_RANGE, "pa_alloc_create: initial order is not a permutation (entry %d)", i);
+    return pa::guard("pa_alloc_create", [&]() -> pa_status {
+        if (!out) return fail(PA_ERR_NULL, "pa_alloc_create: out is NULL");
+        *out = nullptr;
+        if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
+            return fail(PA_ERR_SHAPE, "pa_alloc_create: sizes must be positive");
+        if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+            return fail(PA_ERR_RANGE, "pa_alloc_create: num_blocks*block_size overflows int32 slots");
+        pa_allocator* a = new (std::nothrow) pa_allocator(num_blocks, block_size, max_blocks_per_seq);
+        if (!a) return fail(PA_ERR_RANGE, "pa_alloc_create: out of host memory");
+        if (initial_free_order) {
+            std::vector<char> seen(static_cast<size_t>(num_blocks), 0);
+            for (int32_t i = 0; i < num_blocks; ++i) {
+                int32_t b = initial_free_order[i];
+                if (b < 0 || b >= num_blocks || seen[b]) {
+                    delete a;
+                    return fail(PA_ERR_RANGE, "pa_alloc_create: initial order is not a permutation (entry %d)", i);
+                }
+                seen[b] = 1;
             }
-            seen[b] = 1;
+            for (int32_t i = 0; i < num_blocks; ++i) a->free_list.push_back(initial_free_order[i]);
+        } else {
+            for (int32_t i = 0; i < num_blocks; ++i) a->free_list.push_back(i);
         }
-        for (int32_t i = 0; i < num_blocks; ++i) a->free_list.push_back(initial_free_order[i]);
-    } else {
-        for (int32_t i = 0; i < num_blocks; ++i) a->free_list.push_back(i);
-    }
-    *out = a;
-    return ok();
+        *out = a;
+        return ok();
+    });
 }
 
 void pa_alloc_destroy(pa_allocator* a) { delete a; }
 
 pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq, int32_t n_tokens, int32_t* slots_out) {
-    if (!a) return fail(PA_ERR_NULL, "pa_alloc_add_seq: allocator is NULL");
-    if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq: sequence %lld exists", (long long)seq);
-    if (n_tokens < 0) return fail(PA_ERR_RANGE, "pa_alloc_add_seq: negative token count");
-    int32_t need = (n_tokens + a->block_size - 1) / a->block_size;
-    if (need > a->max_blocks_per_seq)
-        return fail(PA_ERR_SEQ_LIMIT, "pa_alloc_add_seq: %d blocks exceed the per-sequence limit %d", need, a->max_blocks_per_seq);
-    if (need > a->free_list.size())
-        return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_add_seq: need %d blocks, %d free", need, a->free_list.size());
-    Seq s;
-    s.blocks.reserve(static_cast<size_t>(need));
-    for (int32_t i = 0; i < need; ++i) {
-        int32_t b = a->free_list.pop_front();
-        a->refcount[b] = 1;
-        s.blocks.push_back(b);
-    }
-    s.n_tokens = n_tokens;
-    if (slots_out)
-        for (int32_t p = 0; p < n_tokens; ++p) slots_out[p] = a->slot_of(s, p);
-    a->seqs.emplace(seq, std::move(s));
-    return ok();
+    return pa::guard("pa_alloc_add_seq", [&]() -> pa_status {
+        if (!a) return fail(PA_ERR_NULL, "pa_alloc_add_seq: allocator is NULL");
+        if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq: sequence %lld exists", (long long)seq);
+        if (n_tokens < 0) return fail(PA_ERR_RANGE, "pa_alloc_add_seq: negative token count");
+        int32_t need = (n_tokens + a->block_size - 1) / a->block_size;
+        if (need > a->max_blocks_per_seq)
+            return fail(PA_ERR_SEQ_LIMIT, "pa_alloc_add_seq: %d blocks exceed the per-sequence limit %d", need, a->max_blocks_per_seq);
+        if (need > a->free_list.size())
+            return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_add_seq: need %d blocks, %d free", need, a->free_list.size());
+        Seq s;
+        s.blocks.reserve(static_cast<size_t>(need));
+        for (int32_t i = 0; i < need; ++i) {
+            int32_t b = a->free_list.pop_front();
+            a->refcount[b] = 1;
+            s.blocks.push_back(b);
+        }
+        s.n_tokens = n_tokens;
+        if (slots_out)
+            for (int32_t p = 0; p < n_tokens; ++p) slots_out[p] = a->slot_of(s, p);
+        a->seqs.emplace(seq, std::move(s));
+        return ok();
+    });
 }
 
 pa_status pa_alloc_fork(pa_allocator* a, int64_t parent, int64_t child) {
-    if (!a) return fail(PA_ERR_NULL, "pa_alloc_fork: allocator is NULL");
-    auto it = a->seqs.find(parent);
-    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_fork: unknown parent %lld", (long long)parent);
-    if (a->seqs.count(child)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_fork: child %lld exists", (long long)child);
-    Seq copy = it->second;
-    for (int32_t b : copy.blocks) ++a->refcount[b];
-    a->seqs.emplace(child, std::move(copy));
-    return ok();
+    return pa::guard("pa_alloc_fork", [&]() -> pa_status {
+        if (!a) return fail(PA_ERR_NULL, "pa_alloc_fork: allocator is NULL");
+        auto it = a->seqs.find(parent);
+        if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_fork: unknown parent %lld", (long long)parent);
+        if (a->seqs.count(child)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_fork: child %lld exists", (long long)child);
+        Seq copy = it->second;
+        for (int32_t b : copy.blocks) ++a->refcount[b];
+        a->seqs.emplace(child, std::move(copy));
+        return ok();
+    });
 }
 
 static pa_status append_one(pa_allocator* a, int64_t seq, int32_t* slot, int32_t* src, int32_t* dst) {
@@ -222,217 +228,233 @@ static pa_status append_one(pa_allocator* a, int64_t seq, int32_t* slot, int32_t
 }
 
 pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq, int32_t* slot, int32_t* cow_src, int32_t* cow_dst) {
-    if (!a || !slot || !cow_src || !cow_dst) return fail(PA_ERR_NULL, "pa_alloc_append_slot: NULL argument");
-    pa_status st = append_one(a, seq, slot, cow_src, cow_dst);
-    return st == PA_OK ? ok() : st;
+    return pa::guard("pa_alloc_append_slot", [&]() -> pa_status {
+        if (!a || !slot || !cow_src || !cow_dst) return fail(PA_ERR_NULL, "pa_alloc_append_slot: NULL argument");
+        pa_status st = append_one(a, seq, slot, cow_src, cow_dst);
+        return st == PA_OK ? ok() : st;
+    });
 }
 
 pa_status pa_alloc_append_batch(pa_allocator* a, const int64_t* seqs, int32_t n, int32_t* slots_out,
                                 int32_t* cow_pairs_out, int32_t* num_cow, int32_t* num_done) {
-    if (!a || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !num_cow || !num_done)
-        return fail(PA_ERR_NULL, "pa_alloc_append_batch: NULL argument");
-    if (n < 0) return fail(PA_ERR_SHAPE, "pa_alloc_append_batch: negative count");
-    *num_cow = 0;
-    *num_done = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        int32_t src, dst;
-        pa_status st = append_one(a, seqs[i], &slots_out[i], &src, &dst);
-        if (st != PA_OK) return st;
-        if (src >= 0) {
-            cow_pairs_out[2 * *num_cow] = src;
-            cow_pairs_out[2 * *num_cow + 1] = dst;
-            ++*num_cow;
+    return pa::guard("pa_alloc_append_batch", [&]() -> pa_status {
+        if (!a || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !num_cow || !num_done)
+            return fail(PA_ERR_NULL, "pa_alloc_append_batch: NULL argument");
+        if (n < 0) return fail(PA_ERR_SHAPE, "pa_alloc_append_batch: negative count");
+        *num_cow = 0;
+        *num_done = 0;
+        for (int32_t i = 0; i < n; ++i) {
+            int32_t src, dst;
+            pa_status st = append_one(a, seqs[i], &slots_out[i], &src, &dst);
+            if (st != PA_OK) return st;
+            if (src >= 0) {
+                cow_pairs_out[2 * *num_cow] = src;
+                cow_pairs_out[2 * *num_cow + 1] = dst;
+                ++*num_cow;
+            }
+            *num_done = i + 1;
         }
-        *num_done = i + 1;
-    }
-    return ok();
+        return ok();
+    });
 }
 
 pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq) {
-    if (!a) return fail(PA_ERR_NULL, "pa_alloc_free_seq: allocator is NULL");
-    auto it = a->seqs.find(seq);
-    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_free_seq: unknown sequence %lld", (long long)seq);
-    for (int32_t b : it->second.blocks)
-        if (--a->refcount[b] == 0) {
-            a->free_list.push_back(b);
-            auto c = a->cached.find(b);
-            if (c != a->cached.end()) {
-                auto ix = a->prefix_index.find(c->second.hash);
-                if (ix != a->prefix_index.end() && ix->second == b) a->prefix_index.erase(ix);
-                a->cached.erase(c);
+    return pa::guard("pa_alloc_free_seq", [&]() -> pa_status {
+        if (!a) return fail(PA_ERR_NULL, "pa_alloc_free_seq: allocator is NULL");
+        auto it = a->seqs.find(seq);
+        if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_free_seq: unknown sequence %lld", (long long)seq);
+        for (int32_t b : it->second.blocks)
+            if (--a->refcount[b] == 0) {
+                a->free_list.push_back(b);
+                auto c = a->cached.find(b);
+                if (c != a->cached.end()) {
+                    auto ix = a->prefix_index.find(c->second.hash);
+                    if (ix != a->prefix_index.end() && ix->second == b) a->prefix_index.erase(ix);
+                    a->cached.erase(c);
+                }
             }
-        }
-    a->seqs.erase(it);
-    return ok();
+        a->seqs.erase(it);
+        return ok();
+    });
 }
 
 pa_status pa_alloc_add_seq_tokens(pa_allocator* a, int64_t seq, const int32_t* tokens,
                                   int32_t n_tokens, int32_t* slots_out, int32_t* n_cached) {
-    if (!a || !n_cached || (n_tokens > 0 && !tokens))
-        return fail(PA_ERR_NULL, "pa_alloc_add_seq_tokens: NULL argument");
-    if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq_tokens: sequence %lld exists", (long long)seq);
-    if (n_tokens < 0) return fail(PA_ERR_RANGE, "pa_alloc_add_seq_tokens: negative token count");
-    const int32_t bs = a->block_size;
-    const int32_t need = (n_tokens + bs - 1) / bs, full = n_tokens / bs;
-    if (need > a->max_blocks_per_seq)
-        return fail(PA_ERR_SEQ_LIMIT, "pa_alloc_add_seq_tokens: %d blocks exceed the per-sequence limit %d", need, a->max_blocks_per_seq);
-    // Hash every full block; the leading run of matching live blocks is shared.
-    std::vector<uint64_t> hashes(static_cast<size_t>(full));
-    std::vector<int32_t> hits;
-    uint64_t h = 0;
-    int32_t parent = -1;
-    for (int32_t j = 0; j < full; ++j) {
-        const int32_t* tk = tokens + static_cast<size_t>(j) * bs;
-        h = chain_hash(h, tk, bs);
-        hashes[j] = h;
-        if (static_cast<int32_t>(hits.size()) != j) continue;
-        auto ix = a->prefix_index.find(h);
-        if (ix == a->prefix_index.end()) continue;
-        const CachedKey& key = a->cached.at(ix->second);
-        if (key.parent != parent || !std::equal(key.tokens.begin(), key.tokens.end(), tk)) continue;
-        hits.push_back(ix->second);
-        parent = ix->second;
-    }
-    const int32_t n_hit = static_cast<int32_t>(hits.size());
-    if (need - n_hit > a->free_list.size())
-        return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_add_seq_tokens: need %d blocks, %d free", need - n_hit, a->free_list.size());
-    Seq s;
-    s.blocks = hits;
-    for (int32_t b : hits) ++a->refcount[b];
-    parent = n_hit ? hits.back() : -1;
-    for (int32_t j = n_hit; j < need; ++j) {
-        int32_t b = a->free_list.pop_front();
-        a->refcount[b] = 1;
-        s.blocks.push_back(b);
-        if (j < full) {
-            if (!a->prefix_index.count(hashes[j])) {
-                const int32_t* tk = tokens + static_cast<size_t>(j) * bs;
-                a->prefix_index.emplace(hashes[j], b);
-                a->cached[b] = CachedKey{hashes[j], parent, std::vector<int32_t>(tk, tk + bs)};
-            }
-            parent = b;
+    return pa::guard("pa_alloc_add_seq_tokens", [&]() -> pa_status {
+        if (!a || !n_cached || (n_tokens > 0 && !tokens))
+            return fail(PA_ERR_NULL, "pa_alloc_add_seq_tokens: NULL argument");
+        if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq_tokens: sequence %lld exists", (long long)seq);
+        if (n_tokens < 0) return fail(PA_ERR_RANGE, "pa_alloc_add_seq_tokens: negative token count");
+        const int32_t bs = a->block_size;
+        const int32_t need = (n_tokens + bs - 1) / bs, full = n_tokens / bs;
+        if (need > a->max_blocks_per_seq)
+            return fail(PA_ERR_SEQ_LIMIT, "pa_alloc_add_seq_tokens: %d blocks exceed the per-sequence limit %d", need, a->max_blocks_per_seq);
+        // Hash every full block; the leading run of matching live blocks is shared.
+        std::vector<uint64_t> hashes(static_cast<size_t>(full));
+        std::vector<int32_t> hits;
+        uint64_t h = 0;
+        int32_t parent = -1;
+        for (int32_t j = 0; j < full; ++j) {
+            const int32_t* tk = tokens + static_cast<size_t>(j) * bs;
+            h = chain_hash(h, tk, bs);
+            hashes[j] = h;
+            if (static_cast<int32_t>(hits.size()) != j) continue;
+            auto ix = a->prefix_index.find(h);
+            if (ix == a->prefix_index.end()) continue;
+            const CachedKey& key = a->cached.at(ix->second);
+            if (key.parent != parent || !std::equal(key.tokens.begin(), key.tokens.end(), tk)) continue;
+            hits.push_back(ix->second);
+            parent = ix->second;
         }
-    }
-    s.n_tokens = n_tokens;
-    if (slots_out)
-        for (int32_t p = 0; p < n_tokens; ++p) slots_out[p] = a->slot_of(s, p);
-    a->seqs.emplace(seq, std::move(s));
-    a->prefix_queried += n_tokens;
-    a->prefix_hits += static_cast<int64_t>(n_hit) * bs;
-    *n_cached = n_hit * bs;
-    return ok();
+        const int32_t n_hit = static_cast<int32_t>(hits.size());
+        if (need - n_hit > a->free_list.size())
+            return fail(PA_ERR_OUT_OF_BLOCKS, "pa_alloc_add_seq_tokens: need %d blocks, %d free", need - n_hit, a->free_list.size());
+        Seq s;
+        s.blocks = hits;
+        for (int32_t b : hits) ++a->refcount[b];
+        parent = n_hit ? hits.back() : -1;
+        for (int32_t j = n_hit; j < need; ++j) {
+            int32_t b = a->free_list.pop_front();
+            a->refcount[b] = 1;
+            s.blocks.push_back(b);
+            if (j < full) {
+                if (!a->prefix_index.count(hashes[j])) {
+                    const int32_t* tk = tokens + static_cast<size_t>(j) * bs;
+                    a->prefix_index.emplace(hashes[j], b);
+                    a->cached[b] = CachedKey{hashes[j], parent, std::vector<int32_t>(tk, tk + bs)};
+                }
+                parent = b;
+            }
+        }
+        s.n_tokens = n_tokens;
+        if (slots_out)
+            for (int32_t p = 0; p < n_tokens; ++p) slots_out[p] = a->slot_of(s, p);
+        a->seqs.emplace(seq, std::move(s));
+        a->prefix_queried += n_tokens;
+        a->prefix_hits += static_cast<int64_t>(n_hit) * bs;
+        *n_cached = n_hit * bs;
+        return ok();
+    });
 }
 
 pa_status pa_alloc_compact(pa_allocator* a, int32_t* pairs_out, int32_t max_pairs, int32_t* n_pairs) {
-    if (!a || !n_pairs) return fail(PA_ERR_NULL, "pa_alloc_compact: NULL argument");
-    const int32_t nb = a->num_blocks;
-    int32_t used = 0;
-    for (int32_t b = 0; b < nb; ++b) used += a->refcount[b] > 0;
-    // Used blocks at or above `used` pair, in increasing order, with the free
-    // blocks below it; the two lists have equal length.
-    std::vector<int32_t> remap(static_cast<size_t>(nb));
-    for (int32_t b = 0; b < nb; ++b) remap[b] = b;
-    int32_t moves = 0, hole = 0;
-    for (int32_t b = used; b < nb; ++b) {
-        if (a->refcount[b] == 0) continue;
-        while (a->refcount[hole] != 0) ++hole;
-        remap[b] = hole++;
-        ++moves;
-    }
-    *n_pairs = moves;
-    if (moves > max_pairs)
-        return fail(PA_ERR_RANGE, "pa_alloc_compact: %d moves, room for %d", moves, max_pairs);
-    if (moves > 0 && !pairs_out) return fail(PA_ERR_NULL, "pa_alloc_compact: pairs_out is NULL");
-    int32_t k = 0;
-    for (int32_t b = used; b < nb; ++b) {
-        if (remap[b] == b) continue;
-        pairs_out[2 * k] = b;
-        pairs_out[2 * k + 1] = remap[b];
-        ++k;
-        a->refcount[remap[b]] = a->refcount[b];
-        a->refcount[b] = 0;
-    }
-    if (moves > 0) {
-        for (auto& kv : a->seqs)
-            for (int32_t& b : kv.second.blocks) b = remap[b];
-        std::unordered_map<int32_t, CachedKey> cached;
-        cached.reserve(a->cached.size());
-        for (auto& kv : a->cached) {
-            CachedKey key = std::move(kv.second);
-            if (key.parent >= 0) key.parent = remap[key.parent];
-            cached.emplace(remap[kv.first], std::move(key));
+    return pa::guard("pa_alloc_compact", [&]() -> pa_status {
+        if (!a || !n_pairs) return fail(PA_ERR_NULL, "pa_alloc_compact: NULL argument");
+        const int32_t nb = a->num_blocks;
+        int32_t used = 0;
+        for (int32_t b = 0; b < nb; ++b) used += a->refcount[b] > 0;
+        // Used blocks at or above `used` pair, in increasing order, with the free
+        // blocks below it; the two lists have equal length.
+        std::vector<int32_t> remap(static_cast<size_t>(nb));
+        for (int32_t b = 0; b < nb; ++b) remap[b] = b;
+        int32_t moves = 0, hole = 0;
+        for (int32_t b = used; b < nb; ++b) {
+            if (a->refcount[b] == 0) continue;
+            while (a->refcount[hole] != 0) ++hole;
+            remap[b] = hole++;
+            ++moves;
         }
-        a->cached = std::move(cached);
-        for (auto& kv : a->prefix_index) kv.second = remap[kv.second];
-    }
-    a->free_list = FreeList(nb);       // rebuilt in increasing order even with no moves
-    for (int32_t b = used; b < nb; ++b) a->free_list.push_back(b);
-    return ok();
+        *n_pairs = moves;
+        if (moves > max_pairs)
+            return fail(PA_ERR_RANGE, "pa_alloc_compact: %d moves, room for %d", moves, max_pairs);
+        if (moves > 0 && !pairs_out) return fail(PA_ERR_NULL, "pa_alloc_compact: pairs_out is NULL");
+        int32_t k = 0;
+        for (int32_t b = used; b < nb; ++b) {
+            if (remap[b] == b) continue;
+            pairs_out[2 * k] = b;
+            pairs_out[2 * k + 1] = remap[b];
+            ++k;
+            a->refcount[remap[b]] = a->refcount[b];
+            a->refcount[b] = 0;
+        }
+        if (moves > 0) {
+            for (auto& kv : a->seqs)
+                for (int32_t& b : kv.second.blocks) b = remap[b];
+            std::unordered_map<int32_t, CachedKey> cached;
+            cached.reserve(a->cached.size());
+            for (auto& kv : a->cached) {
+                CachedKey key = std::move(kv.second);
+                if (key.parent >= 0) key.parent = remap[key.parent];
+                cached.emplace(remap[kv.first], std::move(key));
+            }
+            a->cached = std::move(cached);
+            for (auto& kv : a->prefix_index) kv.second = remap[kv.second];
+        }
+        a->free_list = FreeList(nb);       // rebuilt in increasing order even with no moves
+        for (int32_t b = used; b < nb; ++b) a->free_list.push_back(b);
+        return ok();
+    });
 }
 
 pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* queried_tokens, int64_t* hit_tokens,
                                 int32_t* cached_blocks) {
-    if (!a || !queried_tokens || !hit_tokens || !cached_blocks)
-        return fail(PA_ERR_NULL, "pa_alloc_prefix_stats: NULL argument");
-    *queried_tokens = a->prefix_queried;
-    *hit_tokens = a->prefix_hits;
-    *cached_blocks = static_cast<int32_t>(a->prefix_index.size());
-    return ok();
+    return pa::guard("pa_alloc_prefix_stats", [&]() -> pa_status {
+        if (!a || !queried_tokens || !hit_tokens || !cached_blocks)
+            return fail(PA_ERR_NULL, "pa_alloc_prefix_stats: NULL argument");
+        *queried_tokens = a->prefix_queried;
+        *hit_tokens = a->prefix_hits;
+        *cached_blocks = static_cast<int32_t>(a->prefix_index.size());
+        return ok();
+    });
 }
 
 pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seqs, int32_t n, int32_t row_stride,
                           int32_t* block_tables_out, int32_t* context_lens_out) {
-    if (!a || (n > 0 && (!seqs || !block_tables_out))) return fail(PA_ERR_NULL, "pa_alloc_export: NULL argument");
-    if (n < 0 || row_stride <= 0) return fail(PA_ERR_SHAPE, "pa_alloc_export: bad sizes");
-    for (int32_t i = 0; i < n; ++i) {          // check everything first
-        auto it = a->seqs.find(seqs[i]);
-        if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_export: unknown sequence %lld", (long long)seqs[i]);
-        if (static_cast<int32_t>(it->second.blocks.size()) > row_stride)
-            return fail(PA_ERR_SHAPE, "pa_alloc_export: sequence %lld has %zu blocks > row stride %d",
-                        (long long)seqs[i], it->second.blocks.size(), row_stride);
-    }
-    for (int32_t i = 0; i < n; ++i) {
-        const Seq& s = a->seqs.find(seqs[i])->second;
-        int32_t* row = block_tables_out + static_cast<size_t>(i) * row_stride;
-        std::copy(s.blocks.begin(), s.blocks.end(), row);
-        std::fill(row + s.blocks.size(), row + row_stride, -1);
-        if (context_lens_out) context_lens_out[i] = s.n_tokens;
-    }
-    return ok();
+    return pa::guard("pa_alloc_export", [&]() -> pa_status {
+        if (!a || (n > 0 && (!seqs || !block_tables_out))) return fail(PA_ERR_NULL, "pa_alloc_export: NULL argument");
+        if (n < 0 || row_stride <= 0) return fail(PA_ERR_SHAPE, "pa_alloc_export: bad sizes");
+        for (int32_t i = 0; i < n; ++i) {          // check everything first
+            auto it = a->seqs.find(seqs[i]);
+            if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_export: unknown sequence %lld", (long long)seqs[i]);
+            if (static_cast<int32_t>(it->second.blocks.size()) > row_stride)
+                return fail(PA_ERR_SHAPE, "pa_alloc_export: sequence %lld has %zu blocks > row stride %d",
+                            (long long)seqs[i], it->second.blocks.size(), row_stride);
+        }
+        for (int32_t i = 0; i < n; ++i) {
+            const Seq& s = a->seqs.find(seqs[i])->second;
+            int32_t* row = block_tables_out + static_cast<size_t>(i) * row_stride;
+            std::copy(s.blocks.begin(), s.blocks.end(), row);
+            std::fill(row + s.blocks.size(), row + row_stride, -1);
+            if (context_lens_out) context_lens_out[i] = s.n_tokens;
+        }
+        return ok();
+    });
 }
 
 pa_status pa_alloc_get_stats(const pa_allocator* a, pa_alloc_stats* out) {
-    if (!a || !out) return fail(PA_ERR_NULL, "pa_alloc_get_stats: NULL argument");
-    std::vector<int32_t> fill(static_cast<size_t>(a->num_blocks), 0);
-    int64_t logical = 0;
-    for (const auto& kv : a->seqs) {
-        const Seq& s = kv.second;
-        logical += s.n_tokens;
-        for (size_t j = 0; j < s.blocks.size(); ++j) {
-            int64_t in_block = static_cast<int64_t>(s.n_tokens) - static_cast<int64_t>(j) * a->block_size;
-            int32_t f = static_cast<int32_t>(std::min<int64_t>(a->block_size, in_block));
-            fill[s.blocks[j]] = std::max(fill[s.blocks[j]], f);
+    return pa::guard("pa_alloc_get_stats", [&]() -> pa_status {
+        if (!a || !out) return fail(PA_ERR_NULL, "pa_alloc_get_stats: NULL argument");
+        std::vector<int32_t> fill(static_cast<size_t>(a->num_blocks), 0);
+        int64_t logical = 0;
+        for (const auto& kv : a->seqs) {
+            const Seq& s = kv.second;
+            logical += s.n_tokens;
+            for (size_t j = 0; j < s.blocks.size(); ++j) {
+                int64_t in_block = static_cast<int64_t>(s.n_tokens) - static_cast<int64_t>(j) * a->block_size;
+                int32_t f = static_cast<int32_t>(std::min<int64_t>(a->block_size, in_block));
+                fill[s.blocks[j]] = std::max(fill[s.blocks[j]], f);
+            }
         }
-    }
-    int32_t used = 0, shared = 0;
-    int64_t filled = 0;
-    for (int32_t b = 0; b < a->num_blocks; ++b) {
-        if (a->refcount[b] > 0) ++used;
-        if (a->refcount[b] > 1) ++shared;
-        filled += fill[b];
-    }
-    out->num_blocks = a->num_blocks;
-    out->free_blocks = a->free_list.size();
-    out->used_blocks = used;
-    out->shared_blocks = shared;
-    out->cow_copies = a->cow_copies;
-    out->live_seqs = static_cast<int64_t>(a->seqs.size());
-    out->logical_tokens = logical;
-    out->stored_tokens = filled;
-    out->utilisation = static_cast<double>(used) / a->num_blocks;
-    const double slots = static_cast<double>(used) * a->block_size;
-    out->internal_fragmentation = used ? (slots - static_cast<double>(filled)) / slots : 0.0;
-    return ok();
+        int32_t used = 0, shared = 0;
+        int64_t filled = 0;
+        for (int32_t b = 0; b < a->num_blocks; ++b) {
+            if (a->refcount[b] > 0) ++used;
+            if (a->refcount[b] > 1) ++shared;
+            filled += fill[b];
+        }
+        out->num_blocks = a->num_blocks;
+        out->free_blocks = a->free_list.size();
+        out->used_blocks = used;
+        out->shared_blocks = shared;
+        out->cow_copies = a->cow_copies;
+        out->live_seqs = static_cast<int64_t>(a->seqs.size());
+        out->logical_tokens = logical;
+        out->stored_tokens = filled;
+        out->utilisation = static_cast<double>(used) / a->num_blocks;
+        const double slots = static_cast<double>(used) * a->block_size;
+        out->internal_fragmentation = used ? (slots - static_cast<double>(filled)) / slots : 0.0;
+        return ok();
+    });
 }
 
 int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block) {
@@ -450,12 +472,14 @@ int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap) {
 }
 
 pa_status pa_alloc_seq_info(const pa_allocator* a, int64_t seq, int32_t* n_tokens, int32_t* n_blocks) {
-    if (!a || !n_tokens || !n_blocks) return fail(PA_ERR_NULL, "pa_alloc_seq_info: NULL argument");
-    auto it = a->seqs.find(seq);
-    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_seq_info: unknown sequence %lld", (long long)seq);
-    *n_tokens = it->second.n_tokens;
-    *n_blocks = static_cast<int32_t>(it->second.blocks.size());
-    return ok();
+    return pa::guard("pa_alloc_seq_info", [&]() -> pa_status {
+        if (!a || !n_tokens || !n_blocks) return fail(PA_ERR_NULL, "pa_alloc_seq_info: NULL argument");
+        auto it = a->seqs.find(seq);
+        if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_seq_info: unknown sequence %lld", (long long)seq);
+        *n_tokens = it->second.n_tokens;
+        *n_blocks = static_cast<int32_t>(it->second.blocks.size());
+        return ok();
+    });
 }
 
 }  // extern "C"

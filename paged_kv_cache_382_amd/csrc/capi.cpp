@@ -17,8 +17,8 @@
 
 namespace pa {
 
-std::string& error_text() {
-    static thread_local std::string text;
+char* error_text() {
+    static thread_local char text[kErrorChars] = {0};
     return text;
 }
 
@@ -119,7 +119,7 @@ using pa::ok;
 
 extern "C" {
 
-const char* pa_last_error(void) { return pa::error_text().c_str(); }
+const char* pa_last_error(void) { return pa::error_text(); }
 
 const char* pa_version(void) { return "0.1.0"; }
 
@@ -132,82 +132,88 @@ int pa_set_validate(int on) {
 pa_status pa_store_kvcache(const void* k, const void* v, const int32_t* slot_mapping,
                            int32_t num_tokens, void* k_cache, void* v_cache,
                            const pa_cache_desc* cache, void* hip_stream) {
-    static const char* fn = "pa_store_kvcache";
-    pa_status st = pa::check_cache(cache, fn);
-    if (st != PA_OK) return st;
-    if (num_tokens < 0) return fail(PA_ERR_SHAPE, "%s: negative num_tokens", fn);
-    if (cache->head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8", fn);
-    if (num_tokens == 0) return ok();
-    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
-    if (!pa::aligned16(k) || !pa::aligned16(v) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache))
-        return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
-    const int64_t total_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
-    const int64_t row_vec16 = static_cast<int64_t>(cache->num_kv_heads) * cache->head_dim / 8;
-    if (row_vec16 > INT32_MAX / 2) return fail(PA_ERR_SHAPE, "%s: row too large", fn);
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (pa::validate_flag()) {
-        std::vector<int32_t> slots;
-        st = pa::fetch(slot_mapping, static_cast<size_t>(num_tokens), slots, stream, fn);
+    return pa::guard("pa_store_kvcache", [&]() -> pa_status {
+        static const char* fn = "pa_store_kvcache";
+        pa_status st = pa::check_cache(cache, fn);
         if (st != PA_OK) return st;
-        std::unordered_set<int32_t> seen;
-        for (int32_t t = 0; t < num_tokens; ++t) {
-            int32_t s = slots[t];
-            if (s < 0) continue;
-            if (s >= total_slots) return fail(PA_ERR_RANGE, "%s: slot %d of token %d out of range", fn, s, t);
-            if (!seen.insert(s).second) return fail(PA_ERR_RANGE, "%s: slot %d written twice", fn, s);
+        if (num_tokens < 0) return fail(PA_ERR_SHAPE, "%s: negative num_tokens", fn);
+        if (cache->head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8", fn);
+        if (num_tokens == 0) return ok();
+        if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+        if (!pa::aligned16(k) || !pa::aligned16(v) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache))
+            return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
+        const int64_t total_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
+        const int64_t row_vec16 = static_cast<int64_t>(cache->num_kv_heads) * cache->head_dim / 8;
+        if (row_vec16 > INT32_MAX / 2) return fail(PA_ERR_SHAPE, "%s: row too large", fn);
+        hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+        if (pa::validate_flag()) {
+            std::vector<int32_t> slots;
+            st = pa::fetch(slot_mapping, static_cast<size_t>(num_tokens), slots, stream, fn);
+            if (st != PA_OK) return st;
+            std::unordered_set<int32_t> seen;
+            for (int32_t t = 0; t < num_tokens; ++t) {
+                int32_t s = slots[t];
+                if (s < 0) continue;
+                if (s >= total_slots) return fail(PA_ERR_RANGE, "%s: slot %d of token %d out of range", fn, s, t);
+                if (!seen.insert(s).second) return fail(PA_ERR_RANGE, "%s: slot %d written twice", fn, s);
+            }
         }
-    }
-    hipError_t err = pa::launch_store_kvcache(k, v, slot_mapping, num_tokens, k_cache, v_cache,
-                                              static_cast<int32_t>(row_vec16), total_slots, stream);
-    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
-    return ok();
+        hipError_t err = pa::launch_store_kvcache(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                                  static_cast<int32_t>(row_vec16), total_slots, stream);
+        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+        return ok();
+    });
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cache,
                          const int32_t* src_dst, int32_t num_pairs, void* hip_stream) {
-    static const char* fn = "pa_copy_blocks";
-    pa_status st = pa::check_cache(cache, fn);
-    if (st != PA_OK) return st;
-    if (num_pairs < 0) return fail(PA_ERR_SHAPE, "%s: negative num_pairs", fn);
-    if (cache->head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8", fn);
-    if (num_pairs == 0) return ok();
-    if (!k_cache || !v_cache || !src_dst) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
-    if (!pa::aligned16(k_cache) || !pa::aligned16(v_cache))
-        return fail(PA_ERR_ALIGN, "%s: caches must be 16-byte aligned", fn);
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (pa::validate_flag()) {
-        std::vector<int32_t> pairs;
-        st = pa::fetch(src_dst, static_cast<size_t>(num_pairs) * 2, pairs, stream, fn);
+    return pa::guard("pa_copy_blocks", [&]() -> pa_status {
+        static const char* fn = "pa_copy_blocks";
+        pa_status st = pa::check_cache(cache, fn);
         if (st != PA_OK) return st;
-        std::unordered_set<int32_t> dsts, srcs;
-        for (int32_t i = 0; i < num_pairs; ++i) {
-            int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
-            if (s < 0 || s >= cache->num_blocks || d < 0 || d >= cache->num_blocks)
-                return fail(PA_ERR_RANGE, "%s: pair %d (%d, %d) out of range", fn, i, s, d);
-            if (!dsts.insert(d).second) return fail(PA_ERR_RANGE, "%s: destination %d repeated", fn, d);
-            srcs.insert(s);
+        if (num_pairs < 0) return fail(PA_ERR_SHAPE, "%s: negative num_pairs", fn);
+        if (cache->head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8", fn);
+        if (num_pairs == 0) return ok();
+        if (!k_cache || !v_cache || !src_dst) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+        if (!pa::aligned16(k_cache) || !pa::aligned16(v_cache))
+            return fail(PA_ERR_ALIGN, "%s: caches must be 16-byte aligned", fn);
+        hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+        if (pa::validate_flag()) {
+            std::vector<int32_t> pairs;
+            st = pa::fetch(src_dst, static_cast<size_t>(num_pairs) * 2, pairs, stream, fn);
+            if (st != PA_OK) return st;
+            std::unordered_set<int32_t> dsts, srcs;
+            for (int32_t i = 0; i < num_pairs; ++i) {
+                int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+                if (s < 0 || s >= cache->num_blocks || d < 0 || d >= cache->num_blocks)
+                    return fail(PA_ERR_RANGE, "%s: pair %d (%d, %d) out of range", fn, i, s, d);
+                if (!dsts.insert(d).second) return fail(PA_ERR_RANGE, "%s: destination %d repeated", fn, d);
+                srcs.insert(s);
+            }
+            for (int32_t d : dsts)
+                if (srcs.count(d)) return fail(PA_ERR_RANGE, "%s: block %d is both source and destination", fn, d);
         }
-        for (int32_t d : dsts)
-            if (srcs.count(d)) return fail(PA_ERR_RANGE, "%s: block %d is both source and destination", fn, d);
-    }
-    const int64_t block_vec16 = static_cast<int64_t>(cache->block_size) * cache->num_kv_heads * cache->head_dim / 8;
-    hipError_t err = pa::launch_copy_blocks(k_cache, v_cache, src_dst, num_pairs, block_vec16,
-                                            cache->num_blocks, stream);
-    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
-    return ok();
+        const int64_t block_vec16 = static_cast<int64_t>(cache->block_size) * cache->num_kv_heads * cache->head_dim / 8;
+        hipError_t err = pa::launch_copy_blocks(k_cache, v_cache, src_dst, num_pairs, block_vec16,
+                                                cache->num_blocks, stream);
+        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+        return ok();
+    });
 }
 
 pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream) {
-    static const char* fn = "pa_read_probe";
-    if (bytes % 16 != 0) return fail(PA_ERR_SHAPE, "%s: bytes (%zu) must be a multiple of 16", fn, bytes);
-    if (bytes == 0) return ok();
-    if (!buf || !sink) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
-    if (!pa::aligned16(buf)) return fail(PA_ERR_ALIGN, "%s: buffer must be 16-byte aligned", fn);
-    if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return fail(PA_ERR_ALIGN, "%s: sink must be 4-byte aligned", fn);
-    hipError_t err = pa::launch_read_probe(buf, static_cast<int64_t>(bytes / 16), sink,
-                                           static_cast<hipStream_t>(hip_stream));
-    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
-    return ok();
+    return pa::guard("pa_read_probe", [&]() -> pa_status {
+        static const char* fn = "pa_read_probe";
+        if (bytes % 16 != 0) return fail(PA_ERR_SHAPE, "%s: bytes (%zu) must be a multiple of 16", fn, bytes);
+        if (bytes == 0) return ok();
+        if (!buf || !sink) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+        if (!pa::aligned16(buf)) return fail(PA_ERR_ALIGN, "%s: buffer must be 16-byte aligned", fn);
+        if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return fail(PA_ERR_ALIGN, "%s: sink must be 4-byte aligned", fn);
+        hipError_t err = pa::launch_read_probe(buf, static_cast<int64_t>(bytes / 16), sink,
+                                               static_cast<hipStream_t>(hip_stream));
+        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+        return ok();
+    });
 }
 
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
@@ -231,84 +237,86 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
                     int32_t num_splits, void* workspace, size_t workspace_bytes,
                     void* hip_stream) {
-    static const char* fn = "pa_decode";
-    pa_status st = pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len,
-                                           num_splits, fn);
-    if (st != PA_OK) return st;
-    if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
-    if (num_seqs == 0) return ok();
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
-        return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
-    if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
-        return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
-    const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
-                                                   max_context_len);
-    int32_t splits = pa::resolve_splits(cache, num_q_heads, num_splits);
-    if (num_splits == 0) {
-        // No more splits than chunks can exist: small batches launch a small grid.
-        const int64_t chunk_bound = static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
-                                    ((max_tokens64 + 15) / 16);
-        splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, chunk_bound)));
-    }
-    const size_t need = pa::workspace_for(cache, num_seqs, num_q_heads, splits);
-    if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
-    if (workspace_bytes < need)
-        return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
-    if (reinterpret_cast<uintptr_t>(workspace) % pa::kAlign != 0)
-        return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-    const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
-    if (pairs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld pairs)", fn, (long long)pairs);
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (pa::validate_flag()) {
-        std::vector<int32_t> lens, tables;
-        st = pa::fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
+    return pa::guard("pa_decode", [&]() -> pa_status {
+        static const char* fn = "pa_decode";
+        pa_status st = pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len,
+                                               num_splits, fn);
         if (st != PA_OK) return st;
-        st = pa::fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
-        if (st != PA_OK) return st;
-        for (int32_t s = 0; s < num_seqs; ++s) {
-            const int32_t L = lens[s];
-            if (L < 0 || L > max_tokens64)
-                return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [0, %lld]", fn, s, L,
-                            (long long)max_tokens64);
-            const int32_t used = (L + cache->block_size - 1) / cache->block_size;
-            for (int32_t j = 0; j < used; ++j) {
-                const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
-                if (b < 0 || b >= cache->num_blocks)
-                    return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
+        if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
+        if (num_seqs == 0) return ok();
+        if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+            return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+        if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
+            return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
+        const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
+                                                       max_context_len);
+        int32_t splits = pa::resolve_splits(cache, num_q_heads, num_splits);
+        if (num_splits == 0) {
+            // No more splits than chunks can exist: small batches launch a small grid.
+            const int64_t chunk_bound = static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
+                                        ((max_tokens64 + 15) / 16);
+            splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, chunk_bound)));
+        }
+        const size_t need = pa::workspace_for(cache, num_seqs, num_q_heads, splits);
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+        if (workspace_bytes < need)
+            return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % pa::kAlign != 0)
+            return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+        const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
+        if (pairs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld pairs)", fn, (long long)pairs);
+        hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+        if (pa::validate_flag()) {
+            std::vector<int32_t> lens, tables;
+            st = pa::fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
+            if (st != PA_OK) return st;
+            st = pa::fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
+            if (st != PA_OK) return st;
+            for (int32_t s = 0; s < num_seqs; ++s) {
+                const int32_t L = lens[s];
+                if (L < 0 || L > max_tokens64)
+                    return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [0, %lld]", fn, s, L,
+                                (long long)max_tokens64);
+                const int32_t used = (L + cache->block_size - 1) / cache->block_size;
+                for (int32_t j = 0; j < used; ++j) {
+                    const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
+                    if (b < 0 || b >= cache->num_blocks)
+                        return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
+                }
             }
         }
-    }
-    pa::DecodeArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint16_t*>(k_cache);
-    a.v_cache = static_cast<const uint16_t*>(v_cache);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.out = static_cast<uint16_t*>(out);
-    {
-        const size_t rows = pa::partial_rows(cache, num_seqs, num_q_heads, splits);
-        char* ws = static_cast<char*>(workspace);
-        a.part_ml = reinterpret_cast<float*>(ws);
-        a.part_o = reinterpret_cast<float*>(ws + pa::round_up(rows * 2 * sizeof(float)));
-    }
-    a.num_blocks = cache->num_blocks;
-    a.block_size = cache->block_size;
-    a.num_kv_heads = cache->num_kv_heads;
-    a.head_dim = cache->head_dim;
-    a.num_q_heads = num_q_heads;
-    a.num_seqs = num_seqs;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.max_tokens = static_cast<int32_t>(max_tokens64);
-    a.num_splits = splits;
-    a.scale_log2 = scale * pa::kLog2e;
-    a.whole_pairs = 0;
-    if (num_splits == 0 && num_seqs <= 64 && max_tokens64 <= pa::kWholePairMaxTokens) {
-        a.whole_pairs = 1;
-        a.num_splits = static_cast<int32_t>(pairs);
-    }
-    hipError_t err = pa::launch_decode(a, stream);
-    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
-    return ok();
+        pa::DecodeArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.k_cache = static_cast<const uint16_t*>(k_cache);
+        a.v_cache = static_cast<const uint16_t*>(v_cache);
+        a.block_tables = block_tables;
+        a.context_lens = context_lens;
+        a.out = static_cast<uint16_t*>(out);
+        {
+            const size_t rows = pa::partial_rows(cache, num_seqs, num_q_heads, splits);
+            char* ws = static_cast<char*>(workspace);
+            a.part_ml = reinterpret_cast<float*>(ws);
+            a.part_o = reinterpret_cast<float*>(ws + pa::round_up(rows * 2 * sizeof(float)));
+        }
+        a.num_blocks = cache->num_blocks;
+        a.block_size = cache->block_size;
+        a.num_kv_heads = cache->num_kv_heads;
+        a.head_dim = cache->head_dim;
+        a.num_q_heads = num_q_heads;
+        a.num_seqs = num_seqs;
+        a.max_blocks_per_seq = max_blocks_per_seq;
+        a.max_tokens = static_cast<int32_t>(max_tokens64);
+        a.num_splits = splits;
+        a.scale_log2 = scale * pa::kLog2e;
+        a.whole_pairs = 0;
+        if (num_splits == 0 && num_seqs <= 64 && max_tokens64 <= pa::kWholePairMaxTokens) {
+            a.whole_pairs = 1;
+            a.num_splits = static_cast<int32_t>(pairs);
+        }
+        hipError_t err = pa::launch_decode(a, stream);
+        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+        return ok();
+    });
 }
 
 pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
@@ -317,79 +325,81 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
                      int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
                      float scale, void* out, void* hip_stream) {
-    static const char* fn = "pa_prefill";
-    pa_status st = pa::check_cache(cache, fn);
-    if (st != PA_OK) return st;
-    if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || max_query_len < 0 || max_context_len < 0)
-        return fail(PA_ERR_SHAPE, "%s: negative size or num_q_heads <= 0", fn);
-    if (num_q_heads % cache->num_kv_heads != 0)
-        return fail(PA_ERR_SHAPE, "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
-                    num_q_heads, cache->num_kv_heads);
-    if (!pa::prefill_supported(cache->head_dim, cache->block_size))
-        return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d / block_size %d not supported (64 or 128; a power of two)",
-                    fn, cache->head_dim, cache->block_size);
-    if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
-    if (!(scale > 0.0f) || scale > 1e30f) return fail(PA_ERR_RANGE, "%s: scale must be positive and finite", fn);
-    if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
-        return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
-    if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
-        return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
-    const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
-                                                   max_context_len);
-    const int64_t rows = static_cast<int64_t>(max_query_len) * (num_q_heads / cache->num_kv_heads);
-    if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads * ((rows + 127) / 128) > INT32_MAX / 2)
-        return fail(PA_ERR_SHAPE, "%s: launch too large", fn);
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    if (pa::validate_flag()) {
-        std::vector<int32_t> lens, starts, tables;
-        st = pa::fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
-        if (st == PA_OK) st = pa::fetch(query_start, static_cast<size_t>(num_seqs) + 1, starts, stream, fn);
-        if (st == PA_OK)
-            st = pa::fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
+    return pa::guard("pa_prefill", [&]() -> pa_status {
+        static const char* fn = "pa_prefill";
+        pa_status st = pa::check_cache(cache, fn);
         if (st != PA_OK) return st;
-        if (starts[0] != 0 || starts[num_seqs] != num_tokens)
-            return fail(PA_ERR_RANGE, "%s: query_start must run from 0 to num_tokens (%d)", fn, num_tokens);
-        for (int32_t s = 0; s < num_seqs; ++s) {
-            const int32_t n = starts[s + 1] - starts[s], L = lens[s];
-            if (n < 0) return fail(PA_ERR_RANGE, "%s: query_start decreases at %d", fn, s);
-            if (n > max_query_len)
-                return fail(PA_ERR_RANGE, "%s: chunk %d has %d rows > max_query_len %d", fn, s, n, max_query_len);
-            if (L < n || L > max_tokens64)
-                return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [%d, %lld]", fn, s, L, n,
-                            (long long)max_tokens64);
-            const int32_t used = (L + cache->block_size - 1) / cache->block_size;
-            for (int32_t j = 0; j < used; ++j) {
-                const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
-                if (b < 0 || b >= cache->num_blocks)
-                    return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
+        if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || max_query_len < 0 || max_context_len < 0)
+            return fail(PA_ERR_SHAPE, "%s: negative size or num_q_heads <= 0", fn);
+        if (num_q_heads % cache->num_kv_heads != 0)
+            return fail(PA_ERR_SHAPE, "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
+                        num_q_heads, cache->num_kv_heads);
+        if (!pa::prefill_supported(cache->head_dim, cache->block_size))
+            return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d / block_size %d not supported (64 or 128; a power of two)",
+                        fn, cache->head_dim, cache->block_size);
+        if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
+        if (!(scale > 0.0f) || scale > 1e30f) return fail(PA_ERR_RANGE, "%s: scale must be positive and finite", fn);
+        if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
+        if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+            return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+        if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
+            return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
+        const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
+                                                       max_context_len);
+        const int64_t rows = static_cast<int64_t>(max_query_len) * (num_q_heads / cache->num_kv_heads);
+        if (static_cast<int64_t>(num_seqs) * cache->num_kv_heads * ((rows + 127) / 128) > INT32_MAX / 2)
+            return fail(PA_ERR_SHAPE, "%s: launch too large", fn);
+        hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+        if (pa::validate_flag()) {
+            std::vector<int32_t> lens, starts, tables;
+            st = pa::fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
+            if (st == PA_OK) st = pa::fetch(query_start, static_cast<size_t>(num_seqs) + 1, starts, stream, fn);
+            if (st == PA_OK)
+                st = pa::fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
+            if (st != PA_OK) return st;
+            if (starts[0] != 0 || starts[num_seqs] != num_tokens)
+                return fail(PA_ERR_RANGE, "%s: query_start must run from 0 to num_tokens (%d)", fn, num_tokens);
+            for (int32_t s = 0; s < num_seqs; ++s) {
+                const int32_t n = starts[s + 1] - starts[s], L = lens[s];
+                if (n < 0) return fail(PA_ERR_RANGE, "%s: query_start decreases at %d", fn, s);
+                if (n > max_query_len)
+                    return fail(PA_ERR_RANGE, "%s: chunk %d has %d rows > max_query_len %d", fn, s, n, max_query_len);
+                if (L < n || L > max_tokens64)
+                    return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [%d, %lld]", fn, s, L, n,
+                                (long long)max_tokens64);
+                const int32_t used = (L + cache->block_size - 1) / cache->block_size;
+                for (int32_t j = 0; j < used; ++j) {
+                    const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
+                    if (b < 0 || b >= cache->num_blocks)
+                        return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
+                }
             }
         }
-    }
-    pa::PrefillArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint16_t*>(k_cache);
-    a.v_cache = static_cast<const uint16_t*>(v_cache);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.query_start = query_start;
-    a.out = static_cast<uint16_t*>(out);
-    a.num_blocks = cache->num_blocks;
-    a.block_size = cache->block_size;
-    a.num_kv_heads = cache->num_kv_heads;
-    a.head_dim = cache->head_dim;
-    a.num_q_heads = num_q_heads;
-    a.num_seqs = num_seqs;
-    a.num_tokens = num_tokens;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.max_tokens = static_cast<int32_t>(max_tokens64);
-    a.max_query_len = max_query_len;
-    a.block_shift = 0;
-    while ((1 << a.block_shift) < cache->block_size) ++a.block_shift;
-    a.scale_log2 = scale * pa::kLog2e;
-    hipError_t err = pa::launch_prefill(a, stream);
-    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
-    return ok();
+        pa::PrefillArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.k_cache = static_cast<const uint16_t*>(k_cache);
+        a.v_cache = static_cast<const uint16_t*>(v_cache);
+        a.block_tables = block_tables;
+        a.context_lens = context_lens;
+        a.query_start = query_start;
+        a.out = static_cast<uint16_t*>(out);
+        a.num_blocks = cache->num_blocks;
+        a.block_size = cache->block_size;
+        a.num_kv_heads = cache->num_kv_heads;
+        a.head_dim = cache->head_dim;
+        a.num_q_heads = num_q_heads;
+        a.num_seqs = num_seqs;
+        a.num_tokens = num_tokens;
+        a.max_blocks_per_seq = max_blocks_per_seq;
+        a.max_tokens = static_cast<int32_t>(max_tokens64);
+        a.max_query_len = max_query_len;
+        a.block_shift = 0;
+        while ((1 << a.block_shift) < cache->block_size) ++a.block_shift;
+        a.scale_log2 = scale * pa::kLog2e;
+        hipError_t err = pa::launch_prefill(a, stream);
+        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+        return ok();
+    });
 }
 
 }  // extern "C"

@@ -169,3 +169,26 @@ def test_read_probe_rejects_bad_arguments(buf, nbytes, sink, code):
 
 def test_read_probe_of_nothing_launches_nothing():
     assert pa.lib().pa_read_probe(None, 0, None, None) == 0
+
+
+def test_host_memory_exhaustion_is_a_status_not_an_abort(tmp_path):
+    """Under a 1 GiB address-space cap, an allocator for 400 million blocks
+    cannot be built: the call returns PA_ERR_HOST with a message instead of
+    letting std::bad_alloc cross the C ABI (which would abort the process)."""
+    import subprocess
+    import sys
+    script = tmp_path / "oom.py"
+    script.write_text(
+        "import ctypes, resource, sys\n"
+        "resource.setrlimit(resource.RLIMIT_AS, (1 << 30, resource.RLIM_INFINITY))\n"
+        "lib = ctypes.CDLL(sys.argv[1])\n"
+        "lib.pa_last_error.restype = ctypes.c_char_p\n"
+        "h = ctypes.c_void_p()\n"
+        "rc = lib.pa_alloc_create(400_000_000, 4, 8, None, ctypes.byref(h))\n"
+        "print(rc, lib.pa_last_error().decode())\n")
+    res = subprocess.run([sys.executable, str(script), pa.LIB_PATH], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rc, msg = res.stdout.strip().split(" ", 1)
+    assert int(rc) == NAMES["HOST"]
+    assert "out of host memory" in msg
