@@ -603,7 +603,15 @@ def main():
         torch.cuda.synchronize()
         graph = gs.elapsed_time(ge) / args.steps
 
-    ceiling = None if args.no_read_ceiling else read_ceiling(list(caches[0]), 5)
+    ceiling = None
+    if not args.no_read_ceiling:
+        # Caches smaller than 1 GiB would be read from the 256 MB last-level
+        # cache: probe a dedicated 2 GiB buffer instead.
+        big = caches[0][0].numel() * 2 >= 1 << 30
+        probe_bufs = list(caches[0]) if big else [torch.empty(1 << 30, dtype=torch.float16, device=dev)]
+        ceiling = read_ceiling(probe_bufs, 5)
+        ceiling["buffers"] = "layer 0's K and V caches" if big else "a dedicated 2 GiB buffer"
+        del probe_bufs
 
     n_dec = decode_bytes(lens, hq, hkv, d, bs)
     n_step = layers * (n_dec + store_bytes(B, hkv, d) + copy_bytes(len(plan.cow_pairs), bs, hkv, d))
