@@ -556,6 +556,12 @@ def main():
                         device=dev).reshape(-1, 2)
     desc = pa.CacheDesc(*shape)
     splits = args.splits                 # 0: the library's choice for this batch
+    if (splits == 0 and B <= 64 and min(lens) == max(lens)
+            and B * hkv >= pa.pa_decode_num_splits(desc, hq, 0)):
+        # The host knows the lengths: all equal, and the pairs alone fill the
+        # device, so the balanced split is one workgroup per (sequence, KV head)
+        # pair and the merge would find nothing; ask for that partition.
+        splits = -1
     ws = pa.decode_workspace(desc, B, hq, splits, dev)
 
     def step(events=None):
@@ -635,7 +641,9 @@ def main():
             "workload": describe(wl, plan),
             "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
             "context_min": min(lens), "context_max": max_ctx, "context_sum": sum(lens),
-            "layers": layers, "num_splits": splits or "auto", "pool_blocks": wl.num_blocks,
+            "layers": layers,
+            "num_splits": {0: "auto", -1: "whole pairs (equal contexts)"}.get(splits, splits),
+            "pool_blocks": wl.num_blocks,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),

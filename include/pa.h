@@ -160,7 +160,12 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  *                  contiguous ranges.  A pair that straddles ranges gets
  *                  fp32 partials (running max, sum, weighted values) from
  *                  each, which a second kernel combines, in range order, into
- *                  the output (online-softmax merge).  Must be in [0, 2^20].
+ *                  the output (online-softmax merge).  Must be in [-1, 2^20]:
+ *                  -1 asks for one workgroup per (sequence, KV head) pair
+ *                  whatever the lengths (at most 64 sequences, else
+ *                  PA_ERR_RANGE) -- for a caller that knows its contexts are
+ *                  of about equal length, where the split is that partition
+ *                  anyway and no merge is needed.
  *                  With 0, at most 64 sequences and max_context_len <= 512,
  *                  each workgroup instead takes one whole (sequence, KV head)
  *                  pair and writes its rows directly: a single launch, no

@@ -77,6 +77,10 @@ int32_t resolve_splits(const pa_cache_desc* c, int32_t num_q_heads, int32_t requ
 // one workgroup per (sequence, KV head) pair: every pair is short, so the
 // grid stays balanced, and no merge launch is needed.
 constexpr int64_t kWholePairMaxTokens = 512;
+// num_splits value asking for one workgroup per pair whatever the lengths: for
+// a caller that knows its contexts are (nearly) equal, where the balanced
+// split is this partition anyway and the merge launch would find nothing.
+constexpr int32_t kWholePairs = -1;
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -106,8 +110,8 @@ pa_status check_decode_shapes(const pa_cache_desc* c, int32_t num_seqs, int32_t 
     if (!decode_supported(c->head_dim, c->block_size, num_q_heads / c->num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d, block_size %d, group %d not supported", fn,
                     c->head_dim, c->block_size, num_q_heads / c->num_kv_heads);
-    if (num_splits < 0 || num_splits > kMaxSplits)
-        return fail(PA_ERR_RANGE, "%s: num_splits must be in [0, %d]", fn, kMaxSplits);
+    if (num_splits < kWholePairs || num_splits > kMaxSplits)
+        return fail(PA_ERR_RANGE, "%s: num_splits must be in [-1, %d]", fn, kMaxSplits);
     return PA_OK;
 }
 
@@ -309,7 +313,10 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
         a.num_splits = splits;
         a.scale_log2 = scale * pa::kLog2e;
         a.whole_pairs = 0;
-        if (num_splits == 0 && num_seqs <= 64 && max_tokens64 <= pa::kWholePairMaxTokens) {
+        if (num_splits == pa::kWholePairs && num_seqs > 64)
+            return fail(PA_ERR_RANGE, "%s: num_splits -1 (whole pairs) takes at most 64 sequences", fn);
+        if (num_splits == pa::kWholePairs ||
+            (num_splits == 0 && num_seqs <= 64 && max_tokens64 <= pa::kWholePairMaxTokens)) {
             a.whole_pairs = 1;
             a.num_splits = static_cast<int32_t>(pairs);
         }

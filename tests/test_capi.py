@@ -63,7 +63,8 @@ NAMES = {v: k for k, v in pa.STATUS.items()}
     (dict(), _desc(d=96), "UNSUPPORTED"),
     (dict(), _desc(bs=4), "UNSUPPORTED"),
     (dict(hq=12), None, "UNSUPPORTED"),            # group 3
-    (dict(split=-1), None, "RANGE"),
+    (dict(split=-2), None, "RANGE"),
+    (dict(split=-1, B=65, ws=0x7000, ws_bytes=1 << 30), None, "RANGE"),   # whole pairs: <= 64 seqs
     (dict(split=(1 << 20) + 1), None, "RANGE"),
     (dict(split=16), None, "WORKSPACE"),
     (dict(split=16, ws=0x7000, ws_bytes=10), None, "WORKSPACE"),

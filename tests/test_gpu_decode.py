@@ -414,3 +414,12 @@ def test_whole_pairs_agree_with_split_path_and_repeat_bitwise():
     ref = oracle_out(p, kc, vc)
     check_close(a, ref, "whole pairs")
     check_close(c, ref, "split path")
+
+
+@pytest.mark.parametrize("lens", [MEDIUM_LENS, [1500] * 6], ids=["ragged", "equal"])
+def test_whole_pairs_requested_for_long_contexts(lens):
+    """num_splits = -1: one workgroup per pair whatever the context lengths."""
+    p = build(MEDIUM, plan_fn=medium_plan(lens=lens))
+    out = run_step(p, num_splits=-1)
+    kc, vc = oracle_caches(p)
+    check_close(out, oracle_out(p, kc, vc), "whole pairs requested")
