@@ -187,9 +187,10 @@ pa_status pa_alloc_fork(pa_allocator* a, int64_t parent, int64_t child) {
         auto it = a->seqs.find(parent);
         if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_fork: unknown parent %lld", (long long)parent);
         if (a->seqs.count(child)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_fork: child %lld exists", (long long)child);
+        // Insert first (the only step that can throw), then count the shares.
         Seq copy = it->second;
-        for (int32_t b : copy.blocks) ++a->refcount[b];
-        a->seqs.emplace(child, std::move(copy));
+        const auto ins = a->seqs.emplace(child, std::move(copy));
+        for (int32_t b : ins.first->second.blocks) ++a->refcount[b];
         return ok();
     });
 }
