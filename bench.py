@@ -2,7 +2,9 @@
 
 A step is the whole hot path for one batch, over every layer: copy-on-write
 block copies (when the allocator asked for any), the store of the step's new
-K/V rows, and paged decode attention (balanced split kernel + merge).  The
+K/V rows, and paged decode attention (a balanced split kernel plus a merge
+kernel, or one workgroup per (sequence, KV head) pair when that fills the
+device or the contexts are short).  The
 block tables, slot mapping and context lengths come from the library's C++
 allocator; its per-step host cost is timed separately (``host_step_us``) since
 it runs on the CPU ahead of the GPU work.
@@ -480,6 +482,19 @@ def prefill_main(args, wl, dev):
     print(json.dumps(result), flush=True)
 
 
+# Longest context for which the library's automatic choice (num_splits 0) runs
+# one workgroup per (sequence, KV head) pair, for batches of at most 64.
+WHOLE_PAIR_MAX_TOKENS = 512
+
+
+def decode_kernel_label(splits, batch, max_ctx):
+    """Which decode kernels one pa_decode call launches for this partition."""
+    whole = splits == -1 or (splits == 0 and batch <= 64 and max_ctx <= WHOLE_PAIR_MAX_TOKENS)
+    if whole:
+        return "pa_decode (one workgroup per (sequence, KV head) pair; no merge kernel)"
+    return "pa_decode (balanced split kernel + merge kernel)"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -653,7 +668,7 @@ def main():
         "decode_us_percentiles": pcts([x * 1e3 for x in dec_ms]),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (balanced split kernel + merge kernel)",
+            "kernel": decode_kernel_label(splits, B, max_ctx),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
