@@ -1,0 +1,153 @@
+"""A serving loop over the whole path, step by step against the oracle.
+
+Admissions prefill their prompt in chunks: each chunk's K/V rows are stored
+through the slot mapping, then the chunk's rows attend causally to the prompt
+so far through the block table (``pa_prefill``); each decode
+step appends one slot per running sequence (copy-on-write copies first when a
+forked sequence writes into a shared, partly filled block), stores the step's
+rows and decodes every running sequence; finished sequences free their blocks,
+which later admissions and appends receive while the blocks still hold a
+finished sequence's rows (and the never-written slots keep a NaN sentinel).
+
+The device side drives the library's C++ allocator and HIP kernels; the oracle
+side drives ``AllocatorModel``, ``store_ref``, ``copy_blocks_ref``,
+``prefill_ref`` and ``decode_ref`` on host copies of the same seeded inputs.
+Every prefill chunk is within the parity bar, and at every step the
+slots, copy pairs, block tables and lengths agree exactly, both caches agree
+bit for bit, and the decode output (the library's own partition and an
+explicit split count, which runs the split and merge kernels) is within the
+parity bar (max-abs 4e-3, mean-abs 5e-4, relative L2 1e-3).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_382_amd as pa
+import workloads as W
+from oracle import AllocatorModel, copy_blocks_ref, decode_ref, prefill_ref, store_ref
+from tests.gpu_problems import DEV, check_close, host_u16, say
+from tests.serving_trace import CASES, next_events
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_serving_loop_matches_oracle_every_step(case):
+    name, hq, hkv, d, bs, nb, M, steps, seed, max_prompt, chunk = case
+    rng = np.random.default_rng(seed)
+    order = W.free_order(nb, seed)
+    cpp = pa.Allocator(nb, bs, M, order)
+    model = AllocatorModel(nb, bs, M, order)
+    shape = (nb, bs, hkv, d)
+    kc = W.nan_sentinel_fp16(shape, DEV)
+    vc = W.nan_sentinel_fp16(shape, DEV)
+    kc_ref, vc_ref = host_u16(kc), host_u16(vc)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    draws = iter(range(1, 1 << 30))
+
+    def values(rows, heads):
+        return W.normal_fp16((rows, heads, d), seed * 1_000_003 + next(draws), DEV)
+
+    def store(k, v, slots):
+        nonlocal kc_ref, vc_ref
+        pa.pa_store_kvcache(k, v, torch.tensor(slots, dtype=torch.int32, device=DEV), kc, vc)
+        kc_ref, vc_ref = store_ref(host_u16(k), host_u16(v), slots, kc_ref, vc_ref)
+
+    def prefill_prompt(seq, slots, step):
+        """Store and attend the prompt chunk by chunk; every chunk against the oracle."""
+        table_dev, _ = cpp.export([seq], M)
+        table_ref, _ = model.export([seq], M)
+        assert np.array_equal(table_dev, np.asarray(table_ref, dtype=np.int32)), f"step {step}: prompt table"
+        table_t = torch.from_numpy(np.ascontiguousarray(table_dev)).to(DEV)
+        n = len(slots)
+        for c0 in range(0, n, chunk):
+            c1 = min(n, c0 + chunk)
+            store(values(c1 - c0, hkv), values(c1 - c0, hkv), slots[c0:c1])
+            q = values(c1 - c0, hq)
+            lens = torch.tensor([c1], dtype=torch.int32, device=DEV)
+            starts = torch.tensor([0, c1 - c0], dtype=torch.int32, device=DEV)
+            out = pa.pa_prefill(q, kc, vc, table_t, lens, starts, scale, max_query_len=c1 - c0,
+                                max_context_len=M * bs)
+            torch.cuda.synchronize()
+            ref = prefill_ref(host_u16(q).view(np.float16), kc_ref.view(np.float16),
+                              vc_ref.view(np.float16), table_ref, [c1], [0, c1 - c0], scale)
+            check_close(out, ref, f"{name} step {step}: prefill of seq {seq} rows {c0}..{c1 - 1}")
+            seen["chunks"] += 1
+
+    live, next_id = [], 0
+    seen = {"admit": 0, "fork": 0, "free": 0, "cow": 0, "recycled": 0, "chunks": 0}
+    ever_held = set()
+
+    def note_blocks(seq, before=()):
+        fresh = set(model.seq_blocks(seq)) - set(before)
+        seen["recycled"] += sum(1 for b in fresh if b in ever_held)
+        ever_held.update(fresh)
+
+    for step in range(steps):
+        events, next_id = next_events(rng, model, live, next_id, max_prompt)
+        for ev in events:
+            if ev[0] == "free":
+                cpp.free_seq(ev[1])
+                model.free_seq(ev[1])
+                live.remove(ev[1])
+            elif ev[0] == "fork":
+                cpp.fork(ev[1], ev[2])
+                model.fork(ev[1], ev[2])
+                live.append(ev[2])
+            else:
+                seq, n = ev[1], ev[2]
+                slots = [int(x) for x in cpp.add_seq(seq, n)]
+                assert slots == model.add_seq(seq, n), f"step {step}: admission slots"
+                note_blocks(seq)
+                say(f"serving {name} step {step}: admit seq {seq} ({n} tokens)")
+                prefill_prompt(seq, slots, step)
+                live.append(seq)
+            seen[ev[0]] += 1
+        if not live:
+            continue
+
+        # The decode step: one slot per running sequence, copies, store, decode.
+        held_before = {s: model.seq_blocks(s) for s in live}
+        slots_dev, pairs_dev = cpp.append_batch(live)
+        slots_ref, pairs_ref = [], []
+        for s in live:
+            slot, src, dst = model.append_slot(s)
+            slots_ref.append(slot)
+            if src >= 0:
+                pairs_ref.append((src, dst))
+            note_blocks(s, held_before[s])
+        assert [int(x) for x in slots_dev] == slots_ref, f"step {step}: slots"
+        assert [tuple(int(y) for y in p) for p in pairs_dev] == pairs_ref, f"step {step}: copy pairs"
+        seen["cow"] += len(pairs_ref)
+        tables_dev, lens_dev = cpp.export(live, M)
+        tables_ref, lens_ref = model.export(live, M)
+        assert np.array_equal(tables_dev, np.asarray(tables_ref, dtype=np.int32)), f"step {step}: tables"
+        assert [int(x) for x in lens_dev] == list(lens_ref), f"step {step}: lengths"
+
+        B = len(live)
+        say(f"serving {name} step {step}: {B} sequences, {len(pairs_ref)} copies, "
+            f"longest {max(lens_ref)} tokens")
+        if pairs_ref:
+            pa.pa_copy_blocks(kc, vc, torch.tensor(pairs_ref, dtype=torch.int32, device=DEV))
+            kc_ref, vc_ref = copy_blocks_ref(kc_ref, vc_ref, pairs_ref)
+        store(values(B, hkv), values(B, hkv), slots_ref)
+        q = values(B, hq)
+        tables_t = torch.from_numpy(np.ascontiguousarray(tables_dev)).to(DEV)
+        lens_t = torch.from_numpy(np.ascontiguousarray(lens_dev)).to(DEV)
+        max_ctx = int(max(lens_ref))
+        out_auto = pa.pa_decode(q, kc, vc, tables_t, lens_t, scale, max_context_len=max_ctx)
+        out_split = pa.pa_decode(q, kc, vc, tables_t, lens_t, scale, max_context_len=max_ctx,
+                                 num_splits=7)
+        torch.cuda.synchronize()
+
+        assert np.array_equal(host_u16(kc), kc_ref), f"step {step}: K cache"
+        assert np.array_equal(host_u16(vc), vc_ref), f"step {step}: V cache"
+        ref = decode_ref(host_u16(q).view(np.float16), kc_ref.view(np.float16),
+                         vc_ref.view(np.float16), tables_ref, lens_ref, scale)
+        check_close(out_auto, ref, f"{name} step {step} (library partition)")
+        check_close(out_split, ref, f"{name} step {step} (7 splits + merge)")
+
+    # The trace exercised what it is for.
+    assert seen["admit"] >= 10 and seen["fork"] >= 5 and seen["free"] >= 10, seen
+    assert seen["cow"] >= 5 and seen["recycled"] >= 20 and seen["chunks"] > seen["admit"], seen
