@@ -135,6 +135,20 @@ def counter_traffic(wl_name, kind="decode"):
     return rec.get("hbm_bytes_per_launch")
 
 
+def counter_lds_conflicts(wl_name):
+    """Share of the decode split kernel's LDS-active cycles stalled on bank
+    conflicts, from the committed rocprofv3 counter pass, or None when the
+    decode source changed since it was taken (or no pass exists)."""
+    path = os.path.join(ROOT, "profiles", f"decode_{wl_name}_lds_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("decode_source_sha256_16") != source_digest(DECODE_SRC):
+        return None
+    return rec.get("lds_bank_conflict_share")
+
+
 def pcts(xs):
     """p10 / median / p90 of a list of timings."""
     return {"p10": round(float(np.percentile(xs, 10)), 4), "median": round(float(np.median(xs)), 4),
@@ -685,6 +699,9 @@ def main():
     }
     if traffic is not None:
         result["roofline"]["traffic_over_algorithmic"] = round(traffic / n_dec, 4)
+    lds = counter_lds_conflicts(wl.name)
+    if lds is not None:
+        result["roofline"]["lds_bank_conflict_share"] = lds
     if ceiling is not None:
         result["read_ceiling"] = ceiling
         result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)

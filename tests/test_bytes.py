@@ -74,8 +74,11 @@ def test_prefill_kv_bytes():
     assert bench.prefill_kv_bytes([2048], 8, 128) == 2048 * 8 * 128 * 4
 
 
-@pytest.mark.parametrize("name", sorted(f for f in os.listdir(os.path.join(os.path.dirname(bench.__file__), "profiles"))
-                                        if f.endswith("_counters.json")))
+PROFILES = os.path.join(os.path.dirname(bench.__file__), "profiles")
+
+
+@pytest.mark.parametrize("name", sorted(f for f in os.listdir(PROFILES)
+                                        if f.endswith("_counters.json") and not f.endswith("_lds_counters.json")))
 def test_committed_counter_runs_reach_the_bench_line(name):
     """Every committed counter summary whose kernel source is unchanged is the
     traffic bench.py reports for its workload."""
@@ -87,3 +90,18 @@ def test_committed_counter_runs_reach_the_bench_line(name):
         pytest.skip(f"{kind} kernel changed since {name} was taken")
     wl_name = f"{kind}_{wl}" if kind == "prefill" else wl
     assert bench.counter_traffic(wl_name, kind) == rec["hbm_bytes_per_launch"]
+
+
+@pytest.mark.parametrize("name", sorted(f for f in os.listdir(PROFILES) if f.endswith("_lds_counters.json")))
+def test_committed_lds_counter_runs_reach_the_bench_line(name):
+    """The bank-conflict share bench.py reports is the committed pass's figure
+    for the split kernel: conflict cycles over LDS-active cycles."""
+    wl = name[len("decode_"):-len("_lds_counters.json")]
+    with open(os.path.join(PROFILES, name)) as f:
+        rec = json.load(f)
+    if rec["decode_source_sha256_16"] != bench.source_digest(bench.DECODE_SRC):
+        pytest.skip(f"decode kernel changed since {name} was taken")
+    k = rec["per_kernel_mean_per_dispatch"][rec["dominant_kernel"]]
+    assert rec["dominant_kernel"].startswith("decode_split_kernel")
+    assert rec["lds_bank_conflict_share"] == pytest.approx(k["SQ_LDS_BANK_CONFLICT"] / k["SQ_LDS_IDX_ACTIVE"], abs=1e-5)
+    assert bench.counter_lds_conflicts(wl) == rec["lds_bank_conflict_share"]
