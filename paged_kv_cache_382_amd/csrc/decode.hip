@@ -563,17 +563,35 @@ void decode_split_kernel(const DecodeArgs a) {
 // Merge the partials of pairs that span several splits, and write the zero
 // rows of empty contexts.  One workgroup of 4 waves per (sequence, KV head)
 // pair; pairs the split kernel wrote whole return at once.
+//
+// A pair's partial output of split v is G*D contiguous floats (slot v + pair).
+// The threads form kS groups of kT = G*D/4 threads: thread (grp, t) takes the
+// 16-byte piece t of splits w0 + grp, w0 + grp + kS, ..., with each split's
+// (max, sum) for the piece's head, and folds them in split order into its own
+// online-softmax state; all of a round's loads (kRound splits of the pair) are
+// issued before the first is used, so a pair of up to kRound splits costs one
+// round trip after the split range is known.  The kS states are then combined
+// in group order through LDS.  Every order is fixed: results are bitwise
+// reproducible.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs a) {
+    constexpr int kO = G * D;                     // outputs of a pair
+    constexpr int kT = kO / 4;                    // threads covering one split's partial
+    constexpr int kS = kThreads / kT > 0 ? kThreads / kT : 1;   // split groups
+    constexpr int kIter = 32 / kS > 16 ? 16 : (32 / kS > 0 ? 32 / kS : 1);   // splits per thread a round
+    constexpr int kRound = kS * kIter;            // splits of the pair a round
+    constexpr int kPasses = (kT + kThreads - 1) / kThreads;     // pieces per thread (G*D > 1024)
+    static_assert(kO % 4 == 0, "pieces of 4 outputs");
+
     const int lane = threadIdx.x & (kWave - 1);
     const int Hkv = a.num_kv_heads;
     const int N = a.num_splits;
     const int s = blockIdx.x / Hkv;
     const int g = blockIdx.x % Hkv;
     const int L = uniform(clamped_len(a, s));
+    const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + g * G) * D;
     if (L == 0) {
-        for (int o = threadIdx.x; o < G * D; o += kThreads)
-            a.out[(static_cast<size_t>(s) * a.num_q_heads + g * G) * D + o] = 0;
+        for (int o = threadIdx.x; o < kO; o += kThreads) a.out[out_row0 + o] = 0;
         return;
     }
     const int nch = chunks_of(L);
@@ -589,107 +607,88 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
     const int64_t first = uniform64(before) * Hkv + static_cast<int64_t>(g) * nch;
     const int w0 = owner_of(first, U, N);
     const int w1 = owner_of(first + nch - 1, U, N);
-    if (w0 == w1) return;                      // written whole by the split kernel
+    if (w0 == w1) return;                         // written whole by the split kernel
+    const int P = w1 - w0 + 1;
+    const bool may_be_empty = U < N;              // some splits then hold no chunk
     auto empty_split = [&](int64_t v) { return v * U / N == (v + 1) * U / N; };
-    // Combine the partials of pair (s, g) from splits w0..w1 (skipping empty
-    // ones), in split order, into its fp16 output rows.  The (max, sum) of
-    // each partial are staged in LDS in batches of kBatch splits; each thread
-    // folds them, with its partial outputs, into a running online-softmax
-    // state for the G*D/256 outputs it owns.
-    {
-        constexpr int kOut = (G * D + kThreads - 1) / kThreads;   // outputs per thread
-        constexpr int kBatch = kWaves * D / 2;                    // splits per LDS batch
-        __shared__ float s_pm[kBatch * G];                        // [kBatch][G] max
-        __shared__ float s_pl[kBatch * G];                        // [kBatch][G] sum
-        const size_t pair = static_cast<size_t>(s) * Hkv + g;
-        const bool may_be_empty = U < N;
-        float rm[kOut], rnum[kOut], rden[kOut];
-#pragma unroll
-        for (int j = 0; j < kOut; ++j) {
-            rm[j] = kNegBig;
-            rnum[j] = 0.f;
-            rden[j] = 0.f;
-        }
-        // The first kU partial outputs of each owned output are loaded before
-        // the (max, sum) staging so that both round trips overlap.
-        constexpr int kU = 8;
-        float po0[kOut][kU];
-#pragma unroll
-        for (int j = 0; j < kOut; ++j) {
-            const int o = threadIdx.x + j * kThreads;
-            const int h = o / D;
-            const int d = o % D;
-#pragma unroll
-            for (int t = 0; t < kU; ++t) {
-                const int v = w0 + t;
-                po0[j][t] = 0.f;
-                if (o < G * D && v <= w1 && (!may_be_empty || !empty_split(v)))
-                    po0[j][t] = a.part_o[((v + pair) * G + h) * D + d];
-            }
-        }
-        for (int b0 = w0; b0 <= w1; b0 += kBatch) {
-            const int nb = w1 - b0 + 1 < kBatch ? w1 - b0 + 1 : kBatch;
-            __syncthreads();                  // the previous batch is done
-            for (int i = threadIdx.x; i < nb * G; i += kThreads) {
-                const int v = b0 + i / G;
-                const int h = i % G;
-                float pm = -__builtin_inff(), pl = 0.f;
-                if (!may_be_empty || !empty_split(v)) {
-                    const size_t r = (v + pair) * G + h;
-                    pm = a.part_ml[r * 2];
-                    pl = a.part_ml[r * 2 + 1];
+    const size_t pair = static_cast<size_t>(s) * Hkv + g;
+
+    __shared__ float s_m[kS][kT], s_l[kS][kT];
+    __shared__ float4 s_o[kS][kT];
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int idx = threadIdx.x + pass * kThreads;
+        const int grp = kS > 1 ? idx / kT : 0;
+        const int t = idx % kT;                   // piece: outputs 4t .. 4t+3
+        const bool on = idx < kS * kT;
+        const int h = (4 * t) / D;
+        float m = kNegBig, l = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r0 = 0; r0 < P; r0 += kRound) {
+            float4 po[kIter];
+            float2 pml[kIter];
+    #pragma unroll
+            for (int k = 0; k < kIter; ++k) {
+                const int i = r0 + grp + k * kS;  // split w0 + i
+                const int64_t v = w0 + i;
+                const bool live = on && i < P && (!may_be_empty || !empty_split(v));
+                po[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                pml[k] = make_float2(-__builtin_inff(), 0.f);
+                if (live) {
+                    const size_t slot = static_cast<size_t>(v) + pair;
+                    po[k] = *reinterpret_cast<const float4*>(a.part_o + slot * kO + 4 * t);
+                    pml[k] = *reinterpret_cast<const float2*>(a.part_ml + (slot * G + h) * 2);
                 }
-                s_pm[i] = pm;
-                s_pl[i] = pl;
             }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < kOut; ++j) {
-                const int o = threadIdx.x + j * kThreads;
-                if (o >= G * D) break;
-                const int h = o / D;
-                const int d = o % D;
-                float bm = rm[j];
-                for (int i = 0; i < nb; ++i) bm = __builtin_fmaxf(bm, s_pm[i * G + h]);
-                const float sc = fast_exp2(rm[j] - bm);
-                float num = rnum[j] * sc, den = rden[j] * sc;
-                for (int i0 = 0; i0 < nb; i0 += kU) {
-                    float po[kU];
-#pragma unroll
-                    for (int t = 0; t < kU; ++t) {
-                        const int i = i0 + t;
-                        if (b0 == w0 && i0 == 0) {
-                            po[t] = po0[j][t];
-                            continue;
-                        }
-                        po[t] = 0.f;
-                        if (i < nb && s_pm[i * G + h] != -__builtin_inff())
-                            po[t] = a.part_o[((b0 + i + pair) * G + h) * D + d];
-                    }
-#pragma unroll
-                    for (int t = 0; t < kU; ++t) {
-                        const int i = i0 + t;
-                        if (i >= nb) break;
-                        const float f = fast_exp2(s_pm[i * G + h] - bm);
-                        den = __builtin_fmaf(f, s_pl[i * G + h], den);
-                        num = __builtin_fmaf(f, po[t], num);
-                    }
-                }
-                rm[j] = bm;
-                rnum[j] = num;
-                rden[j] = den;
+            float mr = m;
+    #pragma unroll
+            for (int k = 0; k < kIter; ++k) mr = __builtin_fmaxf(mr, pml[k].x);
+            const float sc = fast_exp2(m - mr);
+            l *= sc;
+            o.x *= sc;
+            o.y *= sc;
+            o.z *= sc;
+            o.w *= sc;
+    #pragma unroll
+            for (int k = 0; k < kIter; ++k) {
+                // An absent split has max -inf: weight 0 and zero partials.
+                const float f = pml[k].x == -__builtin_inff() ? 0.f : fast_exp2(pml[k].x - mr);
+                l = __builtin_fmaf(f, pml[k].y, l);
+                o.x = __builtin_fmaf(f, po[k].x, o.x);
+                o.y = __builtin_fmaf(f, po[k].y, o.y);
+                o.z = __builtin_fmaf(f, po[k].z, o.z);
+                o.w = __builtin_fmaf(f, po[k].w, o.w);
             }
+            m = mr;
         }
-#pragma unroll
-        for (int j = 0; j < kOut; ++j) {
-            const int o = threadIdx.x + j * kThreads;
-            if (o >= G * D) break;
-            const int h = o / D;
-            const int d = o % D;
-            const float r = rden[j] == 0.f ? 0.f : rnum[j] / rden[j];
-            a.out[(static_cast<size_t>(s) * a.num_q_heads + g * G + h) * D + d] =
-                __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
+        if (on) {
+            s_m[grp][t] = m;
+            s_l[grp][t] = l;
+            s_o[grp][t] = o;
         }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < kT; t += kThreads) {
+        float mm = s_m[0][t];
+    #pragma unroll
+        for (int grp = 1; grp < kS; ++grp) mm = __builtin_fmaxf(mm, s_m[grp][t]);
+        float den = 0.f;
+        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    #pragma unroll
+        for (int grp = 0; grp < kS; ++grp) {
+            const float f = s_m[grp][t] == kNegBig && s_l[grp][t] == 0.f ? 0.f : fast_exp2(s_m[grp][t] - mm);
+            den = __builtin_fmaf(f, s_l[grp][t], den);
+            num.x = __builtin_fmaf(f, s_o[grp][t].x, num.x);
+            num.y = __builtin_fmaf(f, s_o[grp][t].y, num.y);
+            num.z = __builtin_fmaf(f, s_o[grp][t].z, num.z);
+            num.w = __builtin_fmaf(f, s_o[grp][t].w, num.w);
+        }
+        const float r[4] = {num.x, num.y, num.z, num.w};
+        uint16_t hv[4];
+    #pragma unroll
+        for (int e = 0; e < 4; ++e)
+            hv[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(den == 0.f ? 0.f : r[e] / den));
+        *reinterpret_cast<uint2*>(a.out + out_row0 + 4 * t) =
+            make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
     }
 }
 
