@@ -423,3 +423,21 @@ def test_whole_pairs_requested_for_long_contexts(lens):
     out = run_step(p, num_splits=-1)
     kc, vc = oracle_caches(p)
     check_close(out, oracle_out(p, kc, vc), "whole pairs requested")
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("n_split", [300, 5000])
+def test_merge_rounds_head_dim_64(g, n_split):
+    """Head dim 64 with pairs spanning many more splits than one merge round
+    holds (300: about 40-100 splits a pair; 5000: more splits than chunks, so
+    many splits are empty and must be skipped by index)."""
+    lens = [1, 300, 777, 1200, 64]
+    hkv = 2
+    m = max(-(-L // 16) for L in lens)
+    nb = sum(-(-L // 16) for L in lens) + 16
+    wl = W.shrink(W.MIX, name=f"merge64_g{g}", num_seqs=len(lens), num_q_heads=g * hkv, num_kv_heads=hkv,
+                  head_dim=64, block_size=16, num_blocks=nb, max_blocks_per_seq=m, seed=200 + g)
+    p = build(wl, lambda a: W._plain_plan(a, wl, lens))
+    out = run_step(p, num_splits=n_split)
+    kc, vc = oracle_caches(p)
+    check_close(out, oracle_out(p, kc, vc), f"head dim 64, group {g}, {n_split} splits")
