@@ -282,9 +282,10 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
  * permutation of [0, num_blocks) giving its first order, else 0..n-1.
  * Every operation either succeeds completely or fails with the state
  * unchanged, except PA_ERR_HOST (host memory exhausted mid-operation): the
- * allocator must then be destroyed.  Host memory only; one allocator must not
- * be used by two threads
- * at once.  Sequence ids are arbitrary int64 values.
+ * allocator must then be destroyed.  pa_alloc_append_batch is a sequence of
+ * such appends: those before a failing one stay applied (*num_done counts
+ * them).  Host memory only; one allocator must not be used by two threads at
+ * once.  Sequence ids are arbitrary int64 values.
  */
 typedef struct pa_allocator pa_allocator;
 

@@ -177,3 +177,34 @@ def test_allocation_latency_p99_below_1ms():
         a.append_batch(list(range(32)))
         lat.append(time.perf_counter() - t0)
     assert np.percentile(lat, 99) < 1e-3
+
+
+def test_append_batch_failure_keeps_earlier_appends():
+    """A batch that runs out of blocks part-way: the appends before the failing
+    one stay applied, later sequences are untouched, and the state equals the
+    model's after the same single appends."""
+    bs, nb = 4, 10
+    order = W.free_order(nb, 9)
+    cpp = Allocator(nb, bs, 8, order)
+    model = AllocatorModel(nb, bs, 8, order)
+    # Three sequences on full blocks (each append needs a fresh block), two
+    # blocks left: the third append of the batch fails.
+    for s in range(3):
+        cpp.add_seq(s, 2 * bs)
+        model.add_seq(s, 2 * bs)
+    assert cpp.num_free() == model.num_free() == 4
+    cpp.add_seq(9, 2 * bs)                                  # leaves 2 free blocks
+    model.add_seq(9, 2 * bs)
+    with pytest.raises(PaError) as e:
+        cpp.append_batch([0, 1, 2])
+    assert e.value.code == "OUT_OF_BLOCKS"
+    for s in (0, 1):
+        model.append_slot(s)
+    with pytest.raises(AllocError):
+        model.append_slot(2)
+    assert [cpp.seq_len(s) for s in range(3)] == [model.seq_len(s) for s in range(3)] == [2 * bs + 1] * 2 + [2 * bs]
+    assert cpp.num_free() == model.num_free() == 0
+    tables, lens = cpp.export([0, 1, 2, 9], 8)
+    ref_tables, ref_lens = model.export([0, 1, 2, 9], 8)
+    assert np.array_equal(tables, np.asarray(ref_tables, dtype=np.int32))
+    assert list(lens) == list(ref_lens)
