@@ -179,6 +179,11 @@ void decode_split_kernel(const DecodeArgs a) {
     constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;   // blocks per chunk
     constexpr int kPerBlock = LPC / BPC;                  // granules of a chunk per block
     static_assert(BS % RPL == 0, "a load must not straddle two blocks");
+    // The pair's ragged last chunk goes through the load pipeline (its rows
+    // past the context read as zeros through a shortened buffer range) where
+    // that costs no registers: one block per chunk and G <= 4.  Otherwise it
+    // is loaded after the pipeline and its rows are dropped in registers.
+    constexpr bool kFold = BS >= kChunk && G <= 4;
 
     __shared__ float s_acc[kWaves][G][D];
     __shared__ float s_m[kWaves][G];
@@ -256,6 +261,10 @@ void decode_split_kernel(const DecodeArgs a) {
             const int n_local = n_seg > wave ? (n_seg - wave + kWaves - 1) / kWaves : 0;
             const int full_seg = (c1 * kChunk <= L ? c1 : c1 - 1) - c0;
             const int n_full = full_seg > wave ? (full_seg - wave + kWaves - 1) / kWaves : 0;
+            // The pair's ragged last chunk (none when L is a multiple of 16) and
+            // the bytes of its block that hold tokens.
+            const int c_rag = (L % kChunk) ? nch - 1 : -1;
+            const uint32_t rag_bytes = static_cast<uint32_t>(L - ((nch - 1) * kChunk / BS) * BS) * row_bytes;
             const int h0 = g * G;
             const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
             const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
@@ -325,7 +334,11 @@ void decode_split_kernel(const DecodeArgs a) {
                     int blk = __builtin_amdgcn_readlane(ids[e], k & (kWave - 1));
                     const bool blk_ok = blk >= 0;
                     blk = blk_ok ? blk : 0;
-                    const uint32_t range = (live && blk_ok) ? block_bytes : 0u;
+                    uint32_t full = block_bytes;
+                    if constexpr (kFold) {
+                        if (c == c_rag) full = rag_bytes;    // ends at the context's last token
+                    }
+                    const uint32_t range = (live && blk_ok) ? full : 0u;
                     const size_t boff = static_cast<size_t>(blk) * block_bytes;
                     Src r;
                     r.kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + boff), 0, range, kRsrcWord3);
@@ -364,10 +377,18 @@ void decode_split_kernel(const DecodeArgs a) {
                 auto consume = [&](uint4 (&kd)[LPC], uint4 (&vd)[LPC], int k, int k2, bool live2,
                                    auto masked_tag) {
                     constexpr bool kMasked = decltype(masked_tag)::value;
+                    // Rows of the chunk that hold a token.  On the pipelined path
+                    // of a folded kernel only rows past the context (the ragged
+                    // chunk) fail; their K and V read as zeros, and the score is
+                    // masked here.
                     bool ok[LPC];
                     if (kMasked) {
     #pragma unroll
                         for (int i = 0; i < LPC; ++i) ok[i] = source(k, i, true).ok;
+                    } else if (kFold) {
+                        const int rem = L - (c0 + wave + (kw + k) * kWaves) * kChunk;
+    #pragma unroll
+                        for (int i = 0; i < LPC; ++i) ok[i] = i * RPL + row < rem;
                     }
                     float sc[LPC][G];
     #pragma unroll
@@ -383,7 +404,7 @@ void decode_split_kernel(const DecodeArgs a) {
                             d = __builtin_amdgcn_fdot2(qv[h][2], k2h, d, false);
                             d = __builtin_amdgcn_fdot2(qv[h][3], k3, d, false);
                             d = row_sum<LPR>(d) * a.scale_log2;
-                            if (kMasked && !ok[i]) d = -__builtin_inff();
+                            if ((kMasked || kFold) && !ok[i]) d = -__builtin_inff();
                             sc[i][h] = d;
                         }
                     }
@@ -433,22 +454,26 @@ void decode_split_kernel(const DecodeArgs a) {
 
                 using Full = std::integral_constant<bool, false>;
                 using Masked = std::integral_constant<bool, true>;
-                if (!any_bad && nfw > 0) {
+                // Chunks the pipeline takes: every chunk of the window when the
+                // ragged one is folded in, else the full ones.
+                const int npw = kFold ? nw : nfw;
+                if (!any_bad && npw > 0) {
                     // Chunks alternate between two register sets X and Y.  Both
                     // loop bodies are unconditional, so every wait is static.
                     uint4 xk[LPC], xv[LPC], yk[LPC], yv[LPC];
                     issue_chunk(xk, xv, 0, true);
-                    issue_chunk(yk, yv, 1, 1 < nfw);
+                    issue_chunk(yk, yv, 1, 1 < npw);
                     int k = 0;
-                    for (; k + 1 < nfw; k += 2) {
-                        consume(xk, xv, k, k + 2, k + 2 < nfw, Full{});
-                        consume(yk, yv, k + 1, k + 3, k + 3 < nfw, Full{});
+                    for (; k + 1 < npw; k += 2) {
+                        consume(xk, xv, k, k + 2, k + 2 < npw, Full{});
+                        consume(yk, yv, k + 1, k + 3, k + 3 < npw, Full{});
                     }
-                    if (k < nfw) consume(xk, xv, k, k + 2, false, Full{});
+                    if (k < npw) consume(xk, xv, k, k + 2, false, Full{});
                 }
-                // The pair's ragged last chunk, or every chunk of a window with a
-                // bad table entry: rows holding no token are dropped.
-                for (int k = any_bad ? 0 : nfw; k < nw; ++k) {
+                // The pair's ragged last chunk (when not folded), or every chunk
+                // of a window with a bad table entry: rows holding no token are
+                // dropped.
+                for (int k = any_bad ? 0 : npw; k < nw; ++k) {
                     uint4 tk[LPC], tv[LPC];
                     issue_chunk(tk, tv, k, true);
                     consume(tk, tv, k, 0, false, Masked{});
