@@ -61,11 +61,21 @@ typedef enum pa_status {
                                   be partly updated and must be destroyed    */
 } pa_status;
 
+/* Order of the rows inside a block.  Slot-major (the default) keeps each
+ * token slot's KV heads together: [num_blocks][block_size][num_kv_heads]
+ * [head_dim], so that the cache is a flat array of slots (each slot one row of
+ * num_kv_heads * head_dim).  Head-major keeps each KV head's rows of a block
+ * together: [num_blocks][num_kv_heads][block_size][head_dim], one contiguous
+ * block_size * head_dim run per (block, KV head).  Slots, block numbers and
+ * every result are the same in both; only addresses differ. */
+typedef enum { PA_LAYOUT_SLOT_MAJOR = 0, PA_LAYOUT_HEAD_MAJOR = 1 } pa_layout;
+
 typedef struct pa_cache_desc {
     int32_t num_blocks;        /* physical blocks in the pool                 */
     int32_t block_size;        /* token slots per block: 8, 16, 32 or 64      */
     int32_t num_kv_heads;      /* KV heads per token                          */
     int32_t head_dim;          /* 64 or 128                                   */
+    int32_t layout;            /* pa_layout; other values: PA_ERR_UNSUPPORTED */
 } pa_cache_desc;
 
 /* Message describing the last failure on the calling thread ("" if none). */

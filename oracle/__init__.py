@@ -30,7 +30,7 @@ Pin status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_allocator_model.py`` or ``tests/test_prefix_compact_model.py``.
 """
 
-from .store import store_ref, copy_blocks_ref
+from .store import LAYOUTS, copy_blocks_ref, slot_view, store_ref
 from .attention import gather_sequence, decode_ref
 from .prefill import prefill_ref
 from .splitk import decode_splitk_ref

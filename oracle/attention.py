@@ -28,6 +28,8 @@ design notes):
 
 import numpy as np
 
+from .store import slot_view
+
 
 def gather_sequence(cache, table_row, context_len, block_size=None):
     """Logical rows ``[context_len, Hkv, D]`` of one sequence, in logical order.
@@ -53,17 +55,18 @@ def gather_sequence(cache, table_row, context_len, block_size=None):
 
 
 def decode_ref(q, k_cache, v_cache, block_tables, context_lens, scale,
-               return_weights=False):
+               return_weights=False, layout="slot"):
     """fp64 decode attention for every (sequence, query head).
 
     q:             [B, Hq, D] float16
-    k/v_cache:     [NB, bs, Hkv, D] float16
+    k/v_cache:     [NB, bs, Hkv, D] float16 ([NB, Hkv, bs, D] with layout "head")
     block_tables:  [B, M] integers (logical -> physical block)
     context_lens:  [B] integers
     scale:         float (rounded to float32 first, as the kernel receives it)
     Returns out [B, Hq, D] float64, and with ``return_weights`` also a list of
     per-sequence [Hq, L] float64 softmax weights.
     """
+    k_cache, v_cache = slot_view(k_cache, layout), slot_view(v_cache, layout)
     q = np.asarray(q)
     B, Hq, D = q.shape
     num_blocks, bs, Hkv, Dk = k_cache.shape

@@ -28,14 +28,17 @@ Readings where the pages are silent (each is listed in the design notes):
 
 import numpy as np
 
+from .store import slot_view
+
 from .attention import gather_sequence
 
 
-def prefill_ref(q, k_cache, v_cache, block_tables, context_lens, query_start, scale):
+def prefill_ref(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                layout="slot"):
     """fp64 causal attention of every packed query row.
 
     q:             [T, Hq, D] float16, rows of all chunks, packed
-    k/v_cache:     [NB, bs, Hkv, D] float16
+    k/v_cache:     [NB, bs, Hkv, D] float16 ([NB, Hkv, bs, D] with layout "head")
     block_tables:  [B, M] integers
     context_lens:  [B] integers, context length including the chunk
     query_start:   [B + 1] integers, non-decreasing, query_start[0] == 0,
@@ -43,6 +46,7 @@ def prefill_ref(q, k_cache, v_cache, block_tables, context_lens, query_start, sc
     scale:         float (rounded to float32 first)
     Returns out [T, Hq, D] float64.
     """
+    k_cache, v_cache = slot_view(k_cache, layout), slot_view(v_cache, layout)
     q = np.asarray(q)
     T, Hq, D = q.shape
     num_blocks, bs, Hkv, Dk = k_cache.shape

@@ -27,6 +27,21 @@ head, K and V) is copied from ``src`` to ``dst``.
 
 import numpy as np
 
+# Cache layouts.  "slot" (the reading above): cache[num_blocks][block_size]
+# [num_kv_heads][head_dim].  "head": cache[num_blocks][num_kv_heads]
+# [block_size][head_dim] -- the same rows, each (block, KV head) run kept
+# together; the pages fix no order inside a block (the slot numbering and the
+# block table are the same in both).
+LAYOUTS = ("slot", "head")
+
+
+def slot_view(cache, layout="slot"):
+    """``cache`` seen as [num_blocks][block_size][num_kv_heads][head_dim]
+    (a numpy view: writes through it land in ``cache``)."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {LAYOUTS}")
+    return cache if layout == "slot" else np.swapaxes(cache, 1, 2)
+
 
 def _as_u16(a):
     a = np.asarray(a)
@@ -37,17 +52,19 @@ def _as_u16(a):
     raise TypeError(f"expected float16 or uint16 array, got {a.dtype}")
 
 
-def store_ref(k, v, slot_mapping, k_cache, v_cache):
+def store_ref(k, v, slot_mapping, k_cache, v_cache, layout="slot"):
     """Return new (k_cache, v_cache) with each token's rows written to its slot.
 
     k, v:          [N, Hkv, D] float16 (or uint16 bit patterns)
     slot_mapping:  [N] integers; slot < 0 skips the token
-    k_cache, v_cache: [NB, bs, Hkv, D] float16 (or uint16); not modified
-    Returns uint16 arrays (the exact bit patterns).
+    k_cache, v_cache: [NB, bs, Hkv, D] float16 (or uint16), or [NB, Hkv, bs, D]
+                   with layout "head"; not modified
+    Returns uint16 arrays (the exact bit patterns), in the caches' layout.
     """
     k16, v16 = _as_u16(k), _as_u16(v)
-    kc = _as_u16(k_cache).copy()
-    vc = _as_u16(v_cache).copy()
+    kc_out = _as_u16(k_cache).copy()
+    vc_out = _as_u16(v_cache).copy()
+    kc, vc = slot_view(kc_out, layout), slot_view(vc_out, layout)
     num_blocks, block_size, hkv, d = kc.shape
     slots = np.asarray(slot_mapping).astype(np.int64).reshape(-1)
     if k16.shape != (slots.size, hkv, d) or v16.shape != k16.shape:
@@ -65,7 +82,7 @@ def store_ref(k, v, slot_mapping, k_cache, v_cache):
         block, offset = divmod(s, block_size)
         kc[block, offset] = k16[t]
         vc[block, offset] = v16[t]
-    return kc, vc
+    return kc_out, vc_out
 
 
 def copy_blocks_ref(k_cache, v_cache, pairs):

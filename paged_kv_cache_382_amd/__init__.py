@@ -42,7 +42,13 @@ class PaError(RuntimeError):
 
 class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
+
+
+# Cache layouts (pa_layout): "slot" = [num_blocks][block_size][num_kv_heads][head_dim]
+# (the default), "head" = [num_blocks][num_kv_heads][block_size][head_dim].
+LAYOUTS = {"slot": 0, "head": 1}
 
 
 class AllocStats(ctypes.Structure):
@@ -154,17 +160,23 @@ def _dev(t, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def cache_desc(k_cache):
-    nb, bs, hkv, d = k_cache.shape
-    return CacheDesc(nb, bs, hkv, d)
+def cache_desc(k_cache, layout="slot"):
+    """Descriptor of a cache tensor whose dimensions are in ``layout`` order."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    if layout == "slot":
+        nb, bs, hkv, d = k_cache.shape
+    else:
+        nb, hkv, bs, d = k_cache.shape
+    return CacheDesc(nb, bs, hkv, d, LAYOUTS[layout])
 
 
-def pa_store_kvcache(k, v, slot_mapping, k_cache, v_cache, stream=None):
+def pa_store_kvcache(k, v, slot_mapping, k_cache, v_cache, stream=None, layout="slot"):
     """Write k/v [N, Hkv, D] fp16 rows to the cache slots in slot_mapping [N] int32."""
     import torch
     if k_cache.shape != v_cache.shape or k.shape != v.shape:
         raise ValueError("k/v and k_cache/v_cache must have matching shapes")
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, layout)
     n = k.shape[0]
     if k.dim() != 3 or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_dim):
         raise ValueError("k must be [N, num_kv_heads, head_dim]")
@@ -177,10 +189,10 @@ def pa_store_kvcache(k, v, slot_mapping, k_cache, v_cache, stream=None):
         ctypes.byref(desc), _stream(stream)))
 
 
-def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None):
+def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None, layout="slot"):
     """Copy whole blocks src_dst[i][0] -> src_dst[i][1] in both caches."""
     import torch
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, layout)
     n = src_dst.shape[0] if src_dst.numel() else 0
     if src_dst.numel() and (src_dst.dim() != 2 or src_dst.shape[1] != 2):
         raise ValueError("src_dst must be [n, 2]")
@@ -218,7 +230,7 @@ def decode_workspace(desc, num_seqs, num_q_heads, num_splits=0, device="cuda"):
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
-              max_context_len=None, num_splits=0, workspace=None, stream=None):
+              max_context_len=None, num_splits=0, workspace=None, stream=None, layout="slot"):
     """Single-query paged attention; returns ``out`` [B, Hq, D] fp16.
 
     ``max_context_len`` (host int) bounds ``context_lens``; by default the
@@ -228,7 +240,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
     ``decode_workspace``) is allocated when not given.
     """
     import torch
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, layout)
     B, hq, d = q.shape
     M = block_tables.shape[1]
     if max_context_len is None:
@@ -253,7 +265,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
 
 
 def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out=None,
-               max_query_len=None, max_context_len=None, stream=None):
+               max_query_len=None, max_context_len=None, stream=None, layout="slot"):
     """Causal attention of packed prompt chunks; returns ``out`` [T, Hq, D] fp16.
 
     ``query_start`` (device int32 [B + 1]) splits the T rows of ``q`` into the
@@ -264,7 +276,7 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, sca
     width times the block size.
     """
     import torch
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, layout)
     T, hq, d = q.shape
     B, M = block_tables.shape
     if context_lens.numel() != B or query_start.numel() != B + 1:
@@ -308,14 +320,15 @@ class DecodeStepGraph:
     """
 
     def __init__(self, layers, q, k_new, v_new, slot_mapping, block_tables, context_lens, scale,
-                 out, cow_pairs=None, max_context_len=None, num_splits=0):
+                 out, cow_pairs=None, max_context_len=None, num_splits=0, layout="slot"):
         import torch
         self.layers = list(layers)
         self.args = (q, k_new, v_new, slot_mapping, block_tables, context_lens, out, cow_pairs)
         self.scale = float(scale)
         self.max_context_len = max_context_len
+        self.layout = layout
         kc0 = self.layers[0][0]
-        desc = cache_desc(kc0)
+        desc = cache_desc(kc0, layout)
         B, hq = q[0].shape[0], q[0].shape[1]
         self.num_splits = int(num_splits)
         self.workspace = decode_workspace(desc, B, hq, self.num_splits, kc0.device)
@@ -335,11 +348,11 @@ class DecodeStepGraph:
         q, k_new, v_new, slots, tables, lens, out, cows = self.args
         for layer, (kc, vc) in enumerate(self.layers):
             if cows is not None and cows.numel():
-                pa_copy_blocks(kc, vc, cows)
-            pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc)
+                pa_copy_blocks(kc, vc, cows, layout=self.layout)
+            pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc, layout=self.layout)
             pa_decode(q[layer], kc, vc, tables, lens, self.scale, out=out[layer],
                       max_context_len=self.max_context_len, num_splits=self.num_splits,
-                      workspace=self.workspace)
+                      workspace=self.workspace, layout=self.layout)
 
     def replay(self):
         self.graph.replay()

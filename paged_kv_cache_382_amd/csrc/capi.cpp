@@ -47,6 +47,8 @@ pa_status check_cache(const pa_cache_desc* c, const char* fn) {
         return fail(PA_ERR_SHAPE, "%s: cache sizes must be positive", fn);
     if (static_cast<int64_t>(c->num_blocks) * c->block_size > INT32_MAX)
         return fail(PA_ERR_RANGE, "%s: num_blocks * block_size exceeds the int32 slot range", fn);
+    if (c->layout != PA_LAYOUT_SLOT_MAJOR && c->layout != PA_LAYOUT_HEAD_MAJOR)
+        return fail(PA_ERR_UNSUPPORTED, "%s: cache layout %d not supported", fn, c->layout);
     return PA_OK;
 }
 
@@ -125,7 +127,7 @@ extern "C" {
 
 const char* pa_last_error(void) { return pa::error_text(); }
 
-const char* pa_version(void) { return "0.1.0"; }
+const char* pa_version(void) { return "0.2.0"; }
 
 int pa_set_validate(int on) {
     int prev = pa::validate_flag();
@@ -163,7 +165,9 @@ pa_status pa_store_kvcache(const void* k, const void* v, const int32_t* slot_map
             }
         }
         hipError_t err = pa::launch_store_kvcache(k, v, slot_mapping, num_tokens, k_cache, v_cache,
-                                                  static_cast<int32_t>(row_vec16), total_slots, stream);
+                                                  static_cast<int32_t>(row_vec16), total_slots,
+                                                  cache->layout == PA_LAYOUT_HEAD_MAJOR, cache->block_size,
+                                                  cache->head_dim / 8, stream);
         if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
         return ok();
     });
@@ -312,6 +316,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
         a.max_tokens = static_cast<int32_t>(max_tokens64);
         a.num_splits = splits;
         a.scale_log2 = scale * pa::kLog2e;
+        a.head_major = cache->layout == PA_LAYOUT_HEAD_MAJOR;
         a.whole_pairs = 0;
         if (num_splits == pa::kWholePairs && num_seqs > 64)
             return fail(PA_ERR_RANGE, "%s: num_splits -1 (whole pairs) takes at most 64 sequences", fn);
@@ -393,6 +398,7 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
         a.num_blocks = cache->num_blocks;
         a.block_size = cache->block_size;
         a.num_kv_heads = cache->num_kv_heads;
+        a.head_major = cache->layout == PA_LAYOUT_HEAD_MAJOR;
         a.head_dim = cache->head_dim;
         a.num_q_heads = num_q_heads;
         a.num_seqs = num_seqs;

@@ -196,8 +196,10 @@ void decode_split_kernel(const DecodeArgs a) {
     const int Hkv = a.num_kv_heads;
     const int N = a.num_splits;
 
-    const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;   // one slot
-    const uint32_t block_bytes = row_bytes * BS;
+    // Bytes from one token's row of a KV head to the next token's: a whole slot
+    // (slot-major) or one head row (head-major).
+    const uint32_t row_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(Hkv) * D * 2;
+    const uint32_t block_bytes = static_cast<uint32_t>(Hkv) * D * 2 * BS;
     // Per-lane byte offset inside a load: row `row` of the load, 16-byte column `col`.
     const uint32_t lane_off = row * row_bytes + col * 16;
 
@@ -268,8 +270,10 @@ void decode_split_kernel(const DecodeArgs a) {
             const int h0 = g * G;
             const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
             const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
-            const char* kbase = reinterpret_cast<const char*>(a.k_cache) + static_cast<size_t>(g) * D * 2;
-            const char* vbase = reinterpret_cast<const char*>(a.v_cache) + static_cast<size_t>(g) * D * 2;
+            // KV head g's first row in a block.
+            const size_t head_off = static_cast<size_t>(g) * D * 2 * (a.head_major ? BS : 1);
+            const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
+            const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
 
             // This lane's 8 columns of the G query rows.
             half2_t qv[G][4];

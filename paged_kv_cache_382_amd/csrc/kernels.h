@@ -30,6 +30,7 @@ struct DecodeArgs {
     float scale_log2;              // scale * log2(e)
     int32_t whole_pairs;           // 1: workgroup w takes (sequence, KV head) pair w whole
                                    // (N = num_seqs * num_kv_heads, at most 64 sequences, no merge)
+    int32_t head_major;            // 1: cache [NB][Hkv][BS][D], else [NB][BS][Hkv][D]
 };
 
 bool decode_supported(int head_dim, int block_size, int group);
@@ -60,14 +61,18 @@ struct PrefillArgs {
     int32_t tiles_per_seq;         // set by the launcher
     int32_t block_shift;           // log2(block_size)
     float scale_log2;              // scale * log2(e), > 0
+    int32_t head_major;            // 1: cache [NB][Hkv][BS][D], else [NB][BS][Hkv][D]
 };
 
 bool prefill_supported(int head_dim, int block_size);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// head_major: the cache is [NB][Hkv][BS][D] (else [NB][BS][Hkv][D]);
+// head_vec16 = D / 8.
 hipError_t launch_store_kvcache(const void* k, const void* v, const int32_t* slots,
                                 int32_t num_tokens, void* k_cache, void* v_cache,
-                                int32_t row_vec16, int64_t total_slots, hipStream_t stream);
+                                int32_t row_vec16, int64_t total_slots, bool head_major,
+                                int32_t block_size, int32_t head_vec16, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
                               int32_t num_pairs, int64_t block_vec16, int32_t num_blocks,

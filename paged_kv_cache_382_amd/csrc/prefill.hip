@@ -157,8 +157,13 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     const int bmask = (1 << bshift) - 1;
     const int* table = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
     const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;   // bytes per slot
-    const uint16_t* kbase = a.k_cache + static_cast<size_t>(g) * D;
-    const uint16_t* vbase = a.v_cache + static_cast<size_t>(g) * D;
+    // Bytes from one token's row of a KV head to the next token's inside a
+    // block (a whole slot, or one head row when head-major), and head g's first
+    // row in a block.
+    const uint32_t tok_bytes = a.head_major ? D * 2 : row_bytes;
+    const size_t head_off = static_cast<size_t>(g) * D * (a.head_major ? a.block_size : 1);
+    const uint16_t* kbase = a.k_cache + head_off;
+    const uint16_t* vbase = a.v_cache + head_off;
 
     // This thread's fixed key offsets inside a tile: K piece slots and V pairs.
     int koff[kKLoads], kpiece[kKLoads], voff[kVLoads], vpiece[kVLoads];
@@ -197,13 +202,14 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     // (scalar-base loads, no 64-bit vector arithmetic).
     auto piece_ptr = [&](const uint16_t* base, bool ok, int b, int key, int piece) -> const u4* {
         if constexpr (kOff32) {
-            const uint32_t off = (ok ? ((static_cast<uint32_t>(b) << bshift) + (key & bmask)) * row_bytes : 0u) +
+            const uint32_t off = (ok ? (static_cast<uint32_t>(b) << bshift) * row_bytes +
+                                           static_cast<uint32_t>(key & bmask) * tok_bytes : 0u) +
                                  16u * piece;
             return reinterpret_cast<const u4*>(reinterpret_cast<const unsigned char*>(base) + off);
         } else {
-            const size_t slot = ok ? (static_cast<size_t>(b) << bshift) + (key & bmask) : 0;
-            return reinterpret_cast<const u4*>(reinterpret_cast<const unsigned char*>(base) +
-                                               slot * row_bytes + 16u * piece);
+            const size_t off = ok ? (static_cast<size_t>(b) << bshift) * row_bytes +
+                                        static_cast<size_t>(key & bmask) * tok_bytes : 0;
+            return reinterpret_cast<const u4*>(reinterpret_cast<const unsigned char*>(base) + off + 16u * piece);
         }
     };
     // Global loads of one tile into registers; the V pieces of keys that hold

@@ -5,8 +5,9 @@
 // each new token's key and value rows are written to the cache slot named by
 // a per-token slot mapping, with the cache seen as a flat array of slots.
 //
-// Design (store): one token row (num_kv_heads * head_dim fp16, contiguous in both the
-// input and the slot-major cache) is moved as 16-byte words.  grid.x walks
+// Design (store): one token row (num_kv_heads * head_dim fp16, contiguous in the
+// input and in a slot-major cache; in a head-major cache each head's piece goes
+// to that head's run of the block) is moved as 16-byte words.  grid.x walks
 // tokens, grid.y splits a row over 256-lane workgroups so that a large row
 // (8 KiB for 32 heads x 128) still spreads over several CUs.  The data never
 // passes through a floating-point register: NaN payloads are preserved.
@@ -19,13 +20,25 @@ namespace {
 __global__ __launch_bounds__(256) void store_kvcache_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v,
     const int32_t* __restrict__ slots, uint4* __restrict__ k_cache,
-    uint4* __restrict__ v_cache, int32_t row_vec16, int64_t total_slots) {
+    uint4* __restrict__ v_cache, int32_t row_vec16, int64_t total_slots, int32_t head_major,
+    int32_t block_size, int32_t head_vec16) {
     const int32_t t = blockIdx.x;
     const int32_t i = blockIdx.y * 256 + threadIdx.x;
     const int32_t slot = slots[t];
     if (slot < 0 || slot >= total_slots || i >= row_vec16) return;
     const size_t src = static_cast<size_t>(t) * row_vec16 + i;
-    const size_t dst = static_cast<size_t>(slot) * row_vec16 + i;
+    // Word i of the token row is word (i % head_vec16) of KV head i / head_vec16.
+    // Slot-major: the row is contiguous at slot * row.  Head-major: the head's
+    // word sits in its run of block_size rows inside the slot's block.
+    size_t dst = static_cast<size_t>(slot) * row_vec16 + i;
+    if (head_major) {
+        const int32_t blk = slot / block_size;
+        const int32_t off = slot - blk * block_size;
+        const int32_t h = i / head_vec16;
+        const int32_t w = i - h * head_vec16;
+        dst = (static_cast<size_t>(blk) * row_vec16 + static_cast<size_t>(h) * head_vec16) * block_size +
+              static_cast<size_t>(off) * head_vec16 + w;
+    }
     const uint4 kw = k[src];
     const uint4 vw = v[src];
     k_cache[dst] = kw;
@@ -82,13 +95,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 
 hipError_t launch_store_kvcache(const void* k, const void* v, const int32_t* slots,
                                 int32_t num_tokens, void* k_cache, void* v_cache,
-                                int32_t row_vec16, int64_t total_slots, hipStream_t stream) {
+                                int32_t row_vec16, int64_t total_slots, bool head_major,
+                                int32_t block_size, int32_t head_vec16, hipStream_t stream) {
     if (num_tokens <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>(num_tokens), static_cast<unsigned>((row_vec16 + 255) / 256));
     hipLaunchKernelGGL(store_kvcache_kernel, grid, dim3(256), 0, stream,
                        static_cast<const uint4*>(k), static_cast<const uint4*>(v), slots,
                        static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), row_vec16,
-                       total_slots);
+                       total_slots, head_major ? 1 : 0, block_size, head_vec16);
     return hipGetLastError();
 }
 

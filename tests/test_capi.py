@@ -193,3 +193,25 @@ def test_host_memory_exhaustion_is_a_status_not_an_abort(tmp_path):
     rc, msg = res.stdout.strip().split(" ", 1)
     assert int(rc) == NAMES["HOST"]
     assert "out of host memory" in msg
+
+
+@pytest.mark.parametrize("layout", [2, -1])
+def test_unknown_cache_layout_is_rejected_before_any_launch(layout):
+    d = pa.CacheDesc(64, 16, 4, 64, layout)
+    assert call_decode(d) == NAMES["UNSUPPORTED"]
+    assert call_prefill(d) == NAMES["UNSUPPORTED"]
+    f = pa.lib().pa_store_kvcache
+    assert f(0x1000, 0x2000, 0x3000, 4, 0x4000, 0x5000, ctypes.byref(d), None) == NAMES["UNSUPPORTED"]
+    assert pa.lib().pa_copy_blocks(0x1000, 0x2000, ctypes.byref(d), 0x3000, 1, None) == NAMES["UNSUPPORTED"]
+    assert "layout" in pa.lib().pa_last_error().decode()
+
+
+def test_cache_desc_reads_the_shape_in_the_named_layout():
+    class T:
+        shape = (64, 4, 16, 128)       # head-major: [NB][Hkv][BS][D]
+    d = pa.cache_desc(T, "head")
+    assert (d.num_blocks, d.block_size, d.num_kv_heads, d.head_dim, d.layout) == (64, 16, 4, 128, 1)
+    d = pa.cache_desc(T)               # slot-major reading of the same shape
+    assert (d.num_blocks, d.block_size, d.num_kv_heads, d.head_dim, d.layout) == (64, 4, 16, 128, 0)
+    with pytest.raises(ValueError):
+        pa.cache_desc(T, "column")

@@ -32,14 +32,15 @@ from tests.serving_trace import CASES, next_events
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("layout", ["slot", "head"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_serving_loop_matches_oracle_every_step(case):
+def test_serving_loop_matches_oracle_every_step(case, layout):
     name, hq, hkv, d, bs, nb, M, steps, seed, max_prompt, chunk = case
     rng = np.random.default_rng(seed)
     order = W.free_order(nb, seed)
     cpp = pa.Allocator(nb, bs, M, order)
     model = AllocatorModel(nb, bs, M, order)
-    shape = (nb, bs, hkv, d)
+    shape = (nb, bs, hkv, d) if layout == "slot" else (nb, hkv, bs, d)
     kc = W.nan_sentinel_fp16(shape, DEV)
     vc = W.nan_sentinel_fp16(shape, DEV)
     kc_ref, vc_ref = host_u16(kc), host_u16(vc)
@@ -51,8 +52,8 @@ def test_serving_loop_matches_oracle_every_step(case):
 
     def store(k, v, slots):
         nonlocal kc_ref, vc_ref
-        pa.pa_store_kvcache(k, v, torch.tensor(slots, dtype=torch.int32, device=DEV), kc, vc)
-        kc_ref, vc_ref = store_ref(host_u16(k), host_u16(v), slots, kc_ref, vc_ref)
+        pa.pa_store_kvcache(k, v, torch.tensor(slots, dtype=torch.int32, device=DEV), kc, vc, layout=layout)
+        kc_ref, vc_ref = store_ref(host_u16(k), host_u16(v), slots, kc_ref, vc_ref, layout=layout)
 
     def prefill_prompt(seq, slots, step):
         """Store and attend the prompt chunk by chunk; every chunk against the oracle."""
@@ -68,10 +69,10 @@ def test_serving_loop_matches_oracle_every_step(case):
             lens = torch.tensor([c1], dtype=torch.int32, device=DEV)
             starts = torch.tensor([0, c1 - c0], dtype=torch.int32, device=DEV)
             out = pa.pa_prefill(q, kc, vc, table_t, lens, starts, scale, max_query_len=c1 - c0,
-                                max_context_len=M * bs)
+                                max_context_len=M * bs, layout=layout)
             torch.cuda.synchronize()
             ref = prefill_ref(host_u16(q).view(np.float16), kc_ref.view(np.float16),
-                              vc_ref.view(np.float16), table_ref, [c1], [0, c1 - c0], scale)
+                              vc_ref.view(np.float16), table_ref, [c1], [0, c1 - c0], scale, layout=layout)
             check_close(out, ref, f"{name} step {step}: prefill of seq {seq} rows {c0}..{c1 - 1}")
             seen["chunks"] += 1
 
@@ -129,24 +130,24 @@ def test_serving_loop_matches_oracle_every_step(case):
         say(f"serving {name} step {step}: {B} sequences, {len(pairs_ref)} copies, "
             f"longest {max(lens_ref)} tokens")
         if pairs_ref:
-            pa.pa_copy_blocks(kc, vc, torch.tensor(pairs_ref, dtype=torch.int32, device=DEV))
+            pa.pa_copy_blocks(kc, vc, torch.tensor(pairs_ref, dtype=torch.int32, device=DEV), layout=layout)
             kc_ref, vc_ref = copy_blocks_ref(kc_ref, vc_ref, pairs_ref)
         store(values(B, hkv), values(B, hkv), slots_ref)
         q = values(B, hq)
         tables_t = torch.from_numpy(np.ascontiguousarray(tables_dev)).to(DEV)
         lens_t = torch.from_numpy(np.ascontiguousarray(lens_dev)).to(DEV)
         max_ctx = int(max(lens_ref))
-        out_auto = pa.pa_decode(q, kc, vc, tables_t, lens_t, scale, max_context_len=max_ctx)
+        out_auto = pa.pa_decode(q, kc, vc, tables_t, lens_t, scale, max_context_len=max_ctx, layout=layout)
         out_split = pa.pa_decode(q, kc, vc, tables_t, lens_t, scale, max_context_len=max_ctx,
-                                 num_splits=7)
+                                 num_splits=7, layout=layout)
         torch.cuda.synchronize()
 
         assert np.array_equal(host_u16(kc), kc_ref), f"step {step}: K cache"
         assert np.array_equal(host_u16(vc), vc_ref), f"step {step}: V cache"
         ref = decode_ref(host_u16(q).view(np.float16), kc_ref.view(np.float16),
-                         vc_ref.view(np.float16), tables_ref, lens_ref, scale)
-        check_close(out_auto, ref, f"{name} step {step} (library partition)")
-        check_close(out_split, ref, f"{name} step {step} (7 splits + merge)")
+                         vc_ref.view(np.float16), tables_ref, lens_ref, scale, layout=layout)
+        check_close(out_auto, ref, f"{name} {layout}-major step {step} (library partition)")
+        check_close(out_split, ref, f"{name} {layout}-major step {step} (7 splits + merge)")
 
     # The trace exercised what it is for.
     assert seen["admit"] >= 10 and seen["fork"] >= 5 and seen["free"] >= 10, seen

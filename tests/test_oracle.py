@@ -20,7 +20,7 @@ import torch
 import oracle
 import workloads as W
 from oracle import (AllocatorModel, copy_blocks_ref, decode_bruteforce, decode_ref,
-                    decode_splitk_ref, gather_sequence, store_bruteforce, store_ref)
+                    decode_splitk_ref, gather_sequence, store_bruteforce, store_ref, prefill_ref)
 from tests.oracle_problems import after_step, build_problem
 
 TINY_GQA = W.shrink(W.TINY, name="tiny_gqa", num_q_heads=8, num_kv_heads=2)
@@ -352,3 +352,54 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
         bad = decoded(p)
         diff = np.abs(bad - brute)
     assert np.isnan(diff).any() or diff.max() > 1e-3
+
+
+def _head_major(c):
+    return np.ascontiguousarray(np.swapaxes(c, 1, 2))
+
+
+def test_head_major_store_puts_each_head_in_its_block_run():
+    """Brute force on positions: token t's head h lands at [slot // bs, h,
+    slot % bs] of a head-major cache, and nothing else changes."""
+    rng = np.random.default_rng(21)
+    NB, bs, H, D = 5, 4, 3, 8
+    kc = rng.integers(0, 1 << 16, size=(NB, H, bs, D), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, size=(NB, H, bs, D), dtype=np.uint16)
+    slots = [7, -1, 0, 19, 12]
+    k = rng.integers(0, 1 << 16, size=(len(slots), H, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(len(slots), H, D), dtype=np.uint16)
+    k2, v2 = store_ref(k, v, slots, kc, vc, layout="head")
+    expect_k, expect_v = kc.copy(), vc.copy()
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        for h in range(H):
+            for d in range(D):
+                expect_k[s // bs, h, s % bs, d] = k[t, h, d]
+                expect_v[s // bs, h, s % bs, d] = v[t, h, d]
+    assert np.array_equal(k2, expect_k) and np.array_equal(v2, expect_v)
+    # The same writes seen slot-major: storing into the transposed cache.
+    ks, vs = store_ref(k, v, slots, np.swapaxes(kc, 1, 2), np.swapaxes(vc, 1, 2))
+    assert np.array_equal(_head_major(ks), k2) and np.array_equal(_head_major(vs), v2)
+
+
+def test_layouts_give_identical_attention():
+    """The layout only moves rows: decode and prefill over a head-major copy
+    of the caches equal the slot-major results bit for bit."""
+    rng = np.random.default_rng(22)
+    NB, bs, Hkv, D, G = 12, 8, 2, 16, 2
+    kc = rng.standard_normal((NB, bs, Hkv, D)).astype(np.float16)
+    vc = rng.standard_normal((NB, bs, Hkv, D)).astype(np.float16)
+    tables = [[4, 9, 1, 0], [11, 2, 7, 3]]
+    lens = [29, 17]
+    q = rng.standard_normal((2, Hkv * G, D)).astype(np.float16)
+    a = decode_ref(q, kc, vc, tables, lens, 0.25)
+    b = decode_ref(q, _head_major(kc), _head_major(vc), tables, lens, 0.25, layout="head")
+    assert np.array_equal(a, b)
+    qp = rng.standard_normal((7, Hkv * G, D)).astype(np.float16)
+    starts = [0, 4, 7]
+    a = prefill_ref(qp, kc, vc, tables, lens, starts, 0.25)
+    b = prefill_ref(qp, _head_major(kc), _head_major(vc), tables, lens, starts, 0.25, layout="head")
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError):
+        decode_ref(q, kc, vc, tables, lens, 0.25, layout="diagonal")
