@@ -149,6 +149,23 @@ def counter_lds_conflicts(wl_name):
     return rec.get("lds_bank_conflict_share")
 
 
+LAYOUT_NAMES = {"slot": "slot-major [block][token][head][dim]",
+                "head": "head-major [block][head][token][dim]"}
+
+
+def cache_shape(wl, layout):
+    """Shape of one layer's K (or V) cache tensor in ``layout``."""
+    if layout == "head":
+        return (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    return (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+
+
+def counter_stem(wl_name, layout):
+    """Workload stem of the committed counter files for a layout (slot-major
+    files carry no suffix)."""
+    return wl_name if layout == "slot" else f"{wl_name}_head"
+
+
 def pcts(xs):
     """p10 / median / p90 of a list of timings."""
     return {"p10": round(float(np.percentile(xs, 10)), 4), "median": round(float(np.median(xs)), 4),
@@ -198,7 +215,7 @@ def parity_summary(diffs, refs):
     return out
 
 
-def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None):
+def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None, layout="slot"):
     """The fp64 oracle on the host cores: one layer, sequences taken in batch
     order until about ``budget_s`` seconds of work.  With ``out0`` (the GPU's
     output of the same layer) the first pass over the batch is also compared
@@ -220,7 +237,8 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None):
         while elapsed < budget_s and done < 64 * len(lens):
             s = done % len(lens)
             t0 = time.perf_counter()
-            ref = decode_ref(qh[s:s + 1], kh, vh, tables[s:s + 1], lens[s:s + 1], wl.scale)
+            ref = decode_ref(qh[s:s + 1], kh, vh, tables[s:s + 1], lens[s:s + 1], wl.scale,
+                             layout=layout)
             elapsed += time.perf_counter() - t0
             if gpu is not None and done < len(lens):
                 diffs.append(gpu[s] - ref[0])
@@ -346,7 +364,7 @@ def compaction_probe(wl, dev, reps):
         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}), flush=True)
 
 
-def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s, out0=None):
+def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s, out0=None, layout="slot"):
     """The oracle timed on the host: causal rows of the first sequence's
     chunk, each row being single-query attention over its prefix (the
     reduction the prefill oracle is pinned to), until ``budget_s`` passes.
@@ -370,7 +388,8 @@ def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s, out0=None
     while time.perf_counter() - t0 < budget_s and done < chunk:
         j = done
         pos = L - chunk + j
-        ref = prefill_ref(q_host[j:j + 1], k_host, v_host, local, [pos + 1], [0, 1], wl.scale)
+        ref = prefill_ref(q_host[j:j + 1], k_host, v_host, local, [pos + 1], [0, 1], wl.scale,
+                          layout=layout)
         flops += 4 * (pos + 1) * wl.num_q_heads * wl.head_dim
         if gpu is not None:
             diffs.append(gpu[j] - ref[0])
@@ -405,7 +424,7 @@ def prefill_main(args, wl, dev):
         sl = alloc.add_seq(s, ctx)
         slots += list(sl[ctx - chunk:])
     tables_h, lens_h = alloc.export(list(range(B)), wl.max_blocks_per_seq)
-    shape = (wl.num_blocks, bs, hkv, d)
+    shape = cache_shape(wl, args.layout)
     caches = []
     for layer in range(layers):
         g = torch.Generator(device=dev)
@@ -427,11 +446,11 @@ def prefill_main(args, wl, dev):
     def step(events=None):
         for layer in range(layers):
             kc, vc = caches[layer]
-            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots_d, kc, vc)
+            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots_d, kc, vc, layout=args.layout)
             if events is not None:
                 events[layer][0].record()
             pa.pa_prefill(q[layer], kc, vc, tables, lens_d, starts, wl.scale, out=out[layer],
-                          max_query_len=chunk, max_context_len=ctx)
+                          max_query_len=chunk, max_context_len=ctx, layout=args.layout)
             if events is not None:
                 events[layer][1].record()
 
@@ -471,6 +490,7 @@ def prefill_main(args, wl, dev):
             "workload": (f"{wl.name}: {B} sequences, each prefilling the last {chunk}-token chunk "
                          f"of a {ctx}-token prompt; {hq}/{hkv} heads, head_dim {d}, block {bs}"),
             "chunk": chunk, "context": ctx, "layers": layers, "pool_blocks": wl.num_blocks,
+            "cache_layout": LAYOUT_NAMES[args.layout],
             "parallelism": "single GPU",
         },
         "prefill_tokens_per_s": round(T / (step_ms * 1e-3), 1),
@@ -484,7 +504,7 @@ def prefill_main(args, wl, dev):
             "peak": PEAK_FP16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-            "traffic": counter_traffic(wl.name, "prefill"),
+            "traffic": counter_traffic(counter_stem(wl.name, args.layout), "prefill"),
             "flops_per_launch": flops,
             "algorithmic_bytes_per_launch": prefill_kv_bytes(lens, hkv, d) + 2 * T * hq * d * 2,
         },
@@ -492,7 +512,7 @@ def prefill_main(args, wl, dev):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = prefill_cpu_baseline(wl, caches[0][0], caches[0][1], q[0],
                                                       tables_h, lens_h, chunk, args.cpu_budget,
-                                                      out0=out[0])
+                                                      out0=out[0], layout=args.layout)
     print(json.dumps(result), flush=True)
 
 
@@ -515,6 +535,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mha")
+    ap.add_argument("--layout", choices=sorted(LAYOUT_NAMES), default="slot",
+                    help="cache layout: slot-major [block][token][head][dim] (default) or "
+                         "head-major [block][head][token][dim]")
     ap.add_argument("--splits", type=int, default=0,
                     help="pieces the decode work is cut into (0 = library default)")
     ap.add_argument("--layers", type=int, default=None)
@@ -564,7 +587,7 @@ def main():
     max_ctx = max(lens)
     hkv, hq, d, bs = wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.block_size
 
-    shape = (wl.num_blocks, bs, hkv, d)
+    shape = cache_shape(wl, args.layout)
     caches = []
     for layer in range(layers):
         g = torch.Generator(device=dev)
@@ -583,7 +606,7 @@ def main():
     slots = torch.tensor(list(plan.step_slots), dtype=torch.int32, device=dev)
     cows = torch.tensor([list(c) for c in plan.cow_pairs], dtype=torch.int32,
                         device=dev).reshape(-1, 2)
-    desc = pa.CacheDesc(*shape)
+    desc = pa.cache_desc(caches[0][0], args.layout)
     splits = args.splits                 # 0: the library's choice for this batch
     if (splits == 0 and B <= 64 and min(lens) == max(lens)
             and B * hkv >= pa.pa_decode_num_splits(desc, hq, 0)):
@@ -597,12 +620,13 @@ def main():
         for layer in range(layers):
             kc, vc = caches[layer]
             if cows.numel():
-                pa.pa_copy_blocks(kc, vc, cows)
-            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc)
+                pa.pa_copy_blocks(kc, vc, cows, layout=args.layout)
+            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc, layout=args.layout)
             if events is not None:
                 events[layer][0].record()
             pa.pa_decode(q[layer], kc, vc, tables, lens_d, wl.scale, out=out[layer],
-                         max_context_len=max_ctx, num_splits=splits, workspace=ws)
+                         max_context_len=max_ctx, num_splits=splits, workspace=ws,
+                         layout=args.layout)
             if events is not None:
                 events[layer][1].record()
 
@@ -626,7 +650,8 @@ def main():
     graph = None
     if args.graph:
         g = pa.DecodeStepGraph(caches, q, k_new, v_new, slots, tables, lens_d, wl.scale, out,
-                               cow_pairs=cows, max_context_len=max_ctx, num_splits=splits)
+                               cow_pairs=cows, max_context_len=max_ctx, num_splits=splits,
+                               layout=args.layout)
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -652,7 +677,7 @@ def main():
     n_step = layers * (n_dec + store_bytes(B, hkv, d) + copy_bytes(len(plan.cow_pairs), bs, hkv, d))
     value = n_step / (step_ms * 1e-3) / 1e9
     achieved = n_dec / (dec_avg_ms * 1e-3) / 1e9
-    traffic = counter_traffic(wl.name)
+    traffic = counter_traffic(counter_stem(wl.name, args.layout))
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -673,6 +698,7 @@ def main():
             "layers": layers,
             "num_splits": {0: "auto", -1: "whole pairs (equal contexts)"}.get(splits, splits),
             "pool_blocks": wl.num_blocks,
+            "cache_layout": LAYOUT_NAMES[args.layout],
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
@@ -699,7 +725,7 @@ def main():
     }
     if traffic is not None:
         result["roofline"]["traffic_over_algorithmic"] = round(traffic / n_dec, 4)
-    lds = counter_lds_conflicts(wl.name)
+    lds = counter_lds_conflicts(counter_stem(wl.name, args.layout))
     if lds is not None:
         result["roofline"]["lds_bank_conflict_share"] = lds
     if ceiling is not None:
@@ -711,7 +737,7 @@ def main():
                            "decode_tokens_per_s": round(B / (graph * 1e-3), 2)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, plan, caches[0][0], caches[0][1], q[0],
-                                              args.cpu_budget, out0=out[0])
+                                              args.cpu_budget, out0=out[0], layout=args.layout)
     print(json.dumps(result, default=lambda o: o.item() if hasattr(o, "item") else str(o)),
           flush=True)
 
