@@ -30,7 +30,9 @@
  * which flattens the cache into token slots, and of [PA-mem] "PagedAttention:
  * the operating system's memory wisdom", which cuts it into fixed-size
  * blocks): one tensor for keys and one for values, each
- *     fp16 [num_blocks][block_size][num_kv_heads][head_dim], contiguous.
+ *     fp16 [num_blocks][block_size][num_kv_heads][head_dim], contiguous
+ * (slot-major, the default; pa_cache_desc.layout may instead name the
+ * head-major order [num_blocks][num_kv_heads][block_size][head_dim]).
  * Slot s is row (s % block_size) of physical block (s / block_size).
  */
 #ifndef PA_H_
