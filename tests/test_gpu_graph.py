@@ -21,12 +21,13 @@ def plan_fn(a):
     return W.prefix_plan(a, WL, prefix_tokens=496, suffix_range=(5, 60))
 
 
-def make_inputs():
+def make_inputs(layout="slot"):
     alloc = pa.Allocator(WL.num_blocks, WL.block_size, WL.max_blocks_per_seq,
                          W.free_order(WL.num_blocks, WL.seed))
     plan = plan_fn(alloc)
     assert len(plan.cow_pairs) == 1                     # the fork forces one copy
-    shape = (WL.num_blocks, WL.block_size, WL.num_kv_heads, WL.head_dim)
+    shape = ((WL.num_blocks, WL.block_size, WL.num_kv_heads, WL.head_dim) if layout == "slot"
+             else (WL.num_blocks, WL.num_kv_heads, WL.block_size, WL.head_dim))
     B = len(plan.seq_ids)
     caches = [(W.normal_fp16(shape, 100 + 2 * i, DEV), W.normal_fp16(shape, 101 + 2 * i, DEV))
               for i in range(LAYERS)]
@@ -44,32 +45,34 @@ def make_inputs():
     return caches, q, k_new, v_new, meta, plan
 
 
-def eager_step(caches, q, k_new, v_new, meta, out):
+def eager_step(caches, q, k_new, v_new, meta, out, layout="slot"):
     for layer, (kc, vc) in enumerate(caches):
-        pa.pa_copy_blocks(kc, vc, meta["cows"])
-        pa.pa_store_kvcache(k_new[layer], v_new[layer], meta["slots"], kc, vc)
+        pa.pa_copy_blocks(kc, vc, meta["cows"], layout=layout)
+        pa.pa_store_kvcache(k_new[layer], v_new[layer], meta["slots"], kc, vc, layout=layout)
         pa.pa_decode(q[layer], kc, vc, meta["tables"], meta["lens"], WL.scale, out=out[layer],
-                     max_context_len=meta["max_ctx"])
+                     max_context_len=meta["max_ctx"], layout=layout)
 
 
-def test_graph_replays_equal_eager_step():
-    caches, q, k_new, v_new, meta, plan = make_inputs()
+@pytest.mark.parametrize("layout", ["slot", "head"])
+def test_graph_replays_equal_eager_step(layout):
+    caches, q, k_new, v_new, meta, plan = make_inputs(layout)
     pristine = [(kc.clone(), vc.clone()) for kc, vc in caches]
 
     say("graph test: eager step")
     eager_caches = [(kc.clone(), vc.clone()) for kc, vc in pristine]
     out_eager = torch.empty_like(q)
-    eager_step(eager_caches, q, k_new, v_new, meta, out_eager)
+    eager_step(eager_caches, q, k_new, v_new, meta, out_eager, layout)
     torch.cuda.synchronize()
 
     # the eager step itself against the oracle, one layer
     kc0, vc0 = (host_u16(t) for t in pristine[1])
     kc0, vc0 = copy_blocks_ref(kc0, vc0, np.asarray(plan.cow_pairs).reshape(-1, 2))
     kc0, vc0 = store_ref(host_u16(k_new[1]).view(np.float16), host_u16(v_new[1]).view(np.float16),
-                         list(plan.step_slots), kc0, vc0)
+                         list(plan.step_slots), kc0, vc0, layout=layout)
     assert np.array_equal(host_u16(eager_caches[1][0]), kc0)
     ref = decode_ref(host_u16(q[1]).view(np.float16), kc0.view(np.float16), vc0.view(np.float16),
-                     np.asarray(plan.block_tables), np.asarray(plan.context_lens), WL.scale)
+                     np.asarray(plan.block_tables), np.asarray(plan.context_lens), WL.scale,
+                     layout=layout)
     check_close(out_eager[1], ref, "graph test eager layer 1")
 
     say("graph test: capture")
@@ -77,7 +80,7 @@ def test_graph_replays_equal_eager_step():
     out_graph = torch.full_like(q, float("nan"))
     step = pa.DecodeStepGraph(graph_caches, q, k_new, v_new, meta["slots"], meta["tables"],
                               meta["lens"], WL.scale, out_graph, cow_pairs=meta["cows"],
-                              max_context_len=meta["max_ctx"])
+                              max_context_len=meta["max_ctx"], layout=layout)
     other = torch.empty_like(q[0])
     for rep in range(3):
         out_graph.fill_(float("nan"))
@@ -91,6 +94,6 @@ def test_graph_replays_equal_eager_step():
             assert torch.equal(gv.view(torch.int16), ev.view(torch.int16))
         # unrelated eager work between replays
         pa.pa_decode(q[0], eager_caches[0][0], eager_caches[0][1], meta["tables"], meta["lens"],
-                     WL.scale, out=other, max_context_len=meta["max_ctx"])
+                     WL.scale, out=other, max_context_len=meta["max_ctx"], layout=layout)
         _ = (other.float() * 2).sum().item()
         torch.cuda.synchronize()
