@@ -49,7 +49,14 @@
 //    plus a per-lane constant offset.  No LDS round trip, no barrier.
 //  * Software pipelining: the next chunk's K and V loads are issued before
 //    the current chunk is consumed (two register buffers).  The loads carry
-//    the non-temporal hint: every byte is read once per call.
+//    the non-temporal hint: every byte is read once per call.  A pair's
+//    ragged last chunk rides the same pipeline where that costs no registers
+//    (one block per chunk, G <= 4): its block's buffer range ends at the
+//    context's last token, so the rows past it read as zeros and are never
+//    fetched.
+//  * Both cache layouts (slot-major [block][token][head][dim] and head-major
+//    [block][head][token][dim]) run the same code: only the stride between a
+//    head's consecutive token rows and the head's offset in a block differ.
 //  * Each 16-lane row group keeps its own online-softmax stream (running max
 //    m, sum l, fp32 accumulator of its 8 columns), so the per-chunk work
 //    needs only an in-row DPP butterfly for the q.k dot product; the row
