@@ -32,9 +32,9 @@ def test_store_small_bit_exact(wl):
     assert_caches_equal(p)
 
 
-@pytest.mark.parametrize("name", ["mha", "mix", "prefix", "long_bs16"])
+@pytest.mark.parametrize("name", ["mha", "mix", "prefix", "long_bs16", "long_bs8", "long_bs64"])
 def test_store_full_size_bit_exact(name):
-    wl = W.ALL.get(name) or W.long_workload(16)
+    wl = W.ALL.get(name) or W.long_workload(int(name.split("bs")[1]))
     p = build(wl, fill="random")
     if p["cows"].numel():
         say(f"{name}: copy blocks")
