@@ -596,6 +596,473 @@ void decode_split_kernel(const DecodeArgs a) {
     if (start < end) process_split(u, start, end);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core variant for 3 to 8 query heads per KV head (block size >= 16).
+//
+// Same partition, workspace and merge as decode_split_kernel; only the work
+// on a segment differs.  The G query rows of a KV head are the rows of
+// v_mfma_f32_4x4x4_16b_f16 tiles (one set of 4 rows for G <= 4, two for
+// G <= 8; rows past G hold zero queries and are never written), so that the
+// products run on the matrix cores and the vector ALUs only keep the
+// softmax bookkeeping of one score per lane:
+//  * scores.  The instruction holds 16 independent 4x4x4 blocks.  Block
+//    b = 4*tg + p of lane l = 4*b + j pairs token 4*tg + j of the 16-token
+//    chunk with a quarter p of the head dimension: the lane loads 16 bytes
+//    of that token's K row at byte 64*m + 16*p (m = 0 .. D/32-1), which is
+//    the B operand of two k-steps as loaded; the A operand is the matching
+//    query columns, held in registers for the whole segment.  The four
+//    quarters' partial scores are summed across lanes (bits 2 and 3 of the
+//    lane id) so that lane l ends with the score of head p, token 4*tg + j.
+//  * softmax: one running max per head, shared by every lane holding that
+//    head, updated once per chunk (cross-lane max over the 16 tokens); exp2
+//    of the scaled score; the probability is rounded to fp16 (the operand
+//    type) and the row sum adds the rounded values, so numerator and
+//    denominator use the same weights.
+//  * values.  P.V contracts over tokens, so its B operand needs 4 tokens of
+//    one column per lane.  The chunk's V rows are loaded in the natural
+//    layout (16 lanes per 256-byte row), written to a wave-private LDS tile
+//    (rows padded by 64 bytes: the transposing reads hit each bank at most
+//    twice) and read back with ds_read_b64_tr_b16, whose 16-lane transpose
+//    turns 4 rows x 4 columns into the operand of lane l: tokens
+//    4*ks .. 4*ks+3 of column 64*grp + l.  The probabilities reach the A
+//    operand through a 128-byte LDS tile per row set.
+//  * the output accumulator of lane l is column 64*grp + l of all the set's
+//    heads: nothing to reduce at the segment end but the row sums.
+// K and V of the next two chunks stay in flight in registers (two sets) as in
+// the vector kernel; loads past a context or behind a bad table entry go
+// through a shortened or empty buffer range and return zeros.
+// ---------------------------------------------------------------------------
+typedef _Float16 mf_h4 __attribute__((ext_vector_type(4)));
+typedef float mf_f4 __attribute__((ext_vector_type(4)));
+typedef short mf_s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) mf_s4 lds_s4;
+
+template <int G>
+constexpr int mfma_row_sets() { return (G + 3) / 4; }
+
+__device__ __forceinline__ float permswap16_a(float x, float& b) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+    return __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+}
+__device__ __forceinline__ float permswap32_a(float x, float& b) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+    return __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+}
+// Max / sum over the 16 tokens of a chunk held by lanes that differ in bits
+// 0, 1 (token within a group of 4), 4 and 5 (group).  Every lane of the set
+// gets the same bits: each step combines a commutative pair.
+__device__ __forceinline__ float tok_max(float x) {
+    x = __builtin_fmaxf(x, dpp_mov<0xB1>(x));
+    x = __builtin_fmaxf(x, dpp_mov<0x4E>(x));
+    float b;
+    float a = permswap16_a(x, b);
+    x = __builtin_fmaxf(a, b);
+    a = permswap32_a(x, b);
+    return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float tok_sum(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    float b;
+    float a = permswap16_a(x, b);
+    x = a + b;
+    a = permswap32_a(x, b);
+    return a + b;
+}
+
+template <int D, int BS, int G>
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 4
+#endif
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? PA_MFMA_WAVES : 2)))
+void decode_mfma_kernel(const DecodeArgs a) {
+    static_assert(BS >= kChunk, "one block per chunk");
+    constexpr int RS = mfma_row_sets<G>();        // sets of 4 query rows
+    constexpr int KM = D / 32;                    // K loads per chunk (4 or 8 whole rows each)
+    constexpr int SL = D / 8;                     // 16-byte slices of a row
+    constexpr int TPL = kChunk / KM;              // K rows per load
+    constexpr int NG = D / 64;                    // 64-column groups of the output
+    constexpr int LPR = D / 8;                    // lanes per V row (natural layout)
+    constexpr int RPL = kWave / LPR;              // V rows per wave load
+    constexpr int VL = kChunk / RPL;              // V loads per chunk
+    constexpr int VROW = D * 2 + 64;              // padded LDS row of the V tile (bytes)
+
+    __shared__ float s_acc[kWaves][G][D];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    __shared__ __attribute__((aligned(16))) char s_v[kWaves][kChunk * VROW];
+    __shared__ __attribute__((aligned(16))) _Float16 s_p[kWaves][RS][4][kChunk];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int lj = lane & 3;                      // token in group (B, D) / query row (A)
+    const int lp = (lane >> 2) & 3;               // quarter of the head dimension / head after the sum
+    const int ltg = lane >> 4;                    // token group
+    const int Hkv = a.num_kv_heads;
+    const int N = a.num_splits;
+
+    const uint32_t row_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(Hkv) * D * 2;
+    const uint32_t block_bytes = static_cast<uint32_t>(Hkv) * D * 2 * BS;
+    // K loads: lane 4*b + j reads slice b % SL of row j + 4*(b / SL) of the
+    // load's TPL rows -- whole rows per instruction, in the lane order of the
+    // B operand (block b = slice, column j = row).
+    const int k_slice = (lane >> 2) % SL;
+    const uint32_t k_lane_off = static_cast<uint32_t>(lj + 4 * ((lane >> 2) / SL)) * row_bytes + 16 * k_slice;
+    const uint32_t v_lane_off = static_cast<uint32_t>(lane / LPR) * row_bytes + 16 * (lane % LPR);
+    // Token of this lane's score after the slice sum (see consume()).
+    const int t_lane = D == 128 ? 4 * ltg + lj : 8 * ((lane >> 4) & 1) + 4 * (lane >> 5) + lj;
+    char* vtile = &s_v[wave][0];
+    const uint32_t v_wr_off = static_cast<uint32_t>(lane / LPR) * VROW + 16 * (lane % LPR);
+    // Transposing read of lane l = 16*g' + 4*e + q: row e of a 4-row step,
+    // columns 16*g' + 4*q .. +3 of a 64-column group.
+    const uint32_t v_rd_off = static_cast<uint32_t>((lane >> 2) & 3) * VROW + (16 * (lane >> 4) + 4 * (lane & 3)) * 2;
+
+    const bool lens_in_regs = a.num_seqs <= kWave;
+    const int len_reg = (lens_in_regs && lane < a.num_seqs) ? clamped_len(a, lane) : 0;
+    const int64_t incl_reg = wave_incl_scan64(chunks_of(len_reg), lane);
+    const int64_t U = (lens_in_regs ? readlane64(incl_reg, kWave - 1) : chunks_per_head(a, lane)) * Hkv;
+    auto len_of = [&](int sq) {
+        return lens_in_regs ? __builtin_amdgcn_readlane(len_reg, sq) : clamped_len(a, sq);
+    };
+
+    auto process_split = [&](int unit, int64_t start, int64_t end) {
+        int s = 0, L = 0, nch = 0;
+        int64_t seq_base = 0;
+        if (lens_in_regs) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.num_seqs && incl_reg * Hkv > start);
+            if (hit) {
+                const int f = __builtin_ctzll(hit);
+                s = f;
+                L = __builtin_amdgcn_readlane(len_reg, f);
+                nch = chunks_of(L);
+                seq_base = (readlane64(incl_reg, f) - nch) * Hkv;
+            }
+        } else {
+            int64_t base = 0;
+            for (int b0 = 0; b0 < a.num_seqs; b0 += kWave) {
+                const int sl = b0 + lane;
+                const int Ll = sl < a.num_seqs ? clamped_len(a, sl) : 0;
+                const int64_t n = chunks_of(Ll);
+                const int64_t incl = wave_incl_scan64(n, lane);
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(sl < a.num_seqs && (base + incl) * Hkv > start);
+                if (hit) {
+                    const int f = __builtin_ctzll(hit);
+                    s = b0 + f;
+                    L = __builtin_amdgcn_readlane(Ll, f);
+                    nch = chunks_of(L);
+                    seq_base = (base + readlane64(incl, f) - nch) * Hkv;
+                    break;
+                }
+                base += readlane64(incl, kWave - 1);
+            }
+        }
+        if (nch == 0) return;
+        int g = static_cast<int>((start - seq_base) / nch);
+        int c0 = static_cast<int>((start - seq_base) % nch);
+        int64_t pos = start;
+
+        for (;;) {
+            const int c1 = static_cast<int>(nch - c0 < end - pos ? nch : c0 + (end - pos));
+            const int n_seg = c1 - c0;
+            const int n_local = n_seg > wave ? (n_seg - wave + kWaves - 1) / kWaves : 0;
+            const int c_rag = (L % kChunk) ? nch - 1 : -1;
+            const uint32_t rag_bytes = static_cast<uint32_t>(L - ((nch - 1) * kChunk / BS) * BS) * row_bytes;
+            const int h0 = g * G;
+            const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
+            const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
+            const size_t head_off = static_cast<size_t>(g) * D * 2 * (a.head_major ? BS : 1);
+            const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
+            const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
+
+            // A operands of the scores: query row 4*r + lj, the 8 columns of
+            // slice k_slice (k-steps hh = 0, 1 of 4 columns each).
+            mf_h4 qop[RS][2];
+#pragma unroll
+            for (int r = 0; r < RS; ++r) {
+                uint4 w = make_uint4(0u, 0u, 0u, 0u);
+                if (4 * r + lj < G) w = *reinterpret_cast<const uint4*>(a.q + out_row0 + (4 * r + lj) * D + 8 * k_slice);
+                qop[r][0] = __builtin_bit_cast(mf_h4, make_uint2(w.x, w.y));
+                qop[r][1] = __builtin_bit_cast(mf_h4, make_uint2(w.z, w.w));
+            }
+            mf_f4 acc[RS][NG];
+            float m_run[RS], l_run[RS];
+#pragma unroll
+            for (int r = 0; r < RS; ++r) {
+                m_run[r] = kNegBig;
+                l_run[r] = 0.f;
+#pragma unroll
+                for (int n = 0; n < NG; ++n) acc[r][n] = mf_f4{0.f, 0.f, 0.f, 0.f};
+            }
+
+            for (int kw = 0; kw < n_local; kw += kWave) {
+                int ids = -1;
+                {
+                    const int c = c0 + wave + (kw + lane) * kWaves;
+                    if (kw + lane < n_local) {
+                        const int id = trow[c * kChunk / BS];
+                        ids = (id < 0 || id >= a.num_blocks) ? -1 : id;
+                    }
+                }
+                const int nw = n_local - kw < kWave ? n_local - kw : kWave;
+
+                struct Src {
+                    __amdgpu_buffer_rsrc_t kr, vr;
+                    int soff;               // byte offset of the chunk's first row in its block
+                    bool blk_ok;
+                    int rem;                // tokens of the context from the chunk's first on
+                };
+                auto source = [&](int k, bool live) -> Src {
+                    const int c = c0 + wave + (kw + k) * kWaves;
+                    int blk = __builtin_amdgcn_readlane(ids, k & (kWave - 1));
+                    const bool blk_ok = blk >= 0;
+                    blk = blk_ok ? blk : 0;
+                    const uint32_t full = c == c_rag ? rag_bytes : block_bytes;
+                    const uint32_t range = (live && blk_ok) ? full : 0u;
+                    const size_t boff = static_cast<size_t>(blk) * block_bytes;
+                    Src r;
+                    r.kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + boff), 0, range, kRsrcWord3);
+                    r.vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + boff), 0, range, kRsrcWord3);
+                    r.soff = static_cast<int>((static_cast<uint32_t>(c * kChunk) % BS) * row_bytes);
+                    r.blk_ok = blk_ok;
+                    r.rem = L - c * kChunk;
+                    return r;
+                };
+                auto load = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t voff, int soff) {
+                    const uint4 r = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kNonTemporal));
+                    __builtin_amdgcn_sched_barrier(0);
+                    return r;
+                };
+                auto issue_k = [&](uint4 (&kd)[KM], const Src& r) {
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) kd[m] = load(r.kr, k_lane_off, r.soff + static_cast<int>(TPL * m * row_bytes));
+                };
+                auto issue_v = [&](uint4 (&vd)[VL], const Src& r) {
+#pragma unroll
+                    for (int v = 0; v < VL; ++v) vd[v] = load(r.vr, v_lane_off, r.soff + static_cast<int>(RPL * v * row_bytes));
+                };
+
+                auto consume = [&](uint4 (&kd)[KM], uint4 (&vd)[VL], int k, int k2, bool live2) {
+                    const Src cur = source(k, true);
+                    // Scores: partial dot products over slice k_slice, for the
+                    // rows of each load (value 4*m + i: load m, head 4r + i).
+                    mf_f4 sc[RS][KM];
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) {
+                        const mf_h4 b0 = __builtin_bit_cast(mf_h4, make_uint2(kd[m].x, kd[m].y));
+                        const mf_h4 b1 = __builtin_bit_cast(mf_h4, make_uint2(kd[m].z, kd[m].w));
+#pragma unroll
+                        for (int r = 0; r < RS; ++r) {
+                            sc[r][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(qop[r][0], b0, mf_f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            sc[r][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(qop[r][1], b1, sc[r][m], 0, 0, 0);
+                        }
+                    }
+                    const Src nxt = source(k2, live2);
+                    issue_k(kd, nxt);
+                    const bool need_mask = !cur.blk_ok || (c0 + wave + (kw + k) * kWaves) == c_rag;
+                    const bool tok_ok = cur.blk_ok && t_lane < cur.rem;
+                    const bool b3 = lp & 2, b2 = lp & 1;
+                    float pr[RS];
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) {
+                        // Sum the slices across lanes, halving the values held
+                        // at each step: lane bit 5 (D = 128 only) keeps loads
+                        // {0,1} or {2,3}, bit 4 one load, bit 3 heads {0,1} or
+                        // {2,3}, bit 2 one head.  Each lane ends with one score:
+                        // head lp of token t_lane.
+                        float y[2][4];
+                        if constexpr (KM == 4) {
+#pragma unroll
+                            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    // Copy the elements out first: this compiler's bit_cast
+                                    // of a vector element reads element 0 whatever the index.
+                                    const float e0 = sc[r][m][i], e1 = sc[r][m + 2][i];
+                                    const unsigned u0 = __builtin_bit_cast(unsigned, e0);
+                                    const unsigned u1 = __builtin_bit_cast(unsigned, e1);
+                                    const auto x = __builtin_amdgcn_permlane32_swap(u0, u1, false, false);
+                                    y[m][i] = __builtin_bit_cast(float, static_cast<unsigned>(x[0])) +
+                                              __builtin_bit_cast(float, static_cast<unsigned>(x[1]));
+                                }
+                        } else {
+#pragma unroll
+                            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) y[m][i] = sc[r][m][i];
+                        }
+                        float z[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const unsigned u0 = __builtin_bit_cast(unsigned, y[0][i]);
+                            const unsigned u1 = __builtin_bit_cast(unsigned, y[1][i]);
+                            const auto x = __builtin_amdgcn_permlane16_swap(u0, u1, false, false);
+                            z[i] = __builtin_bit_cast(float, static_cast<unsigned>(x[0])) +
+                                   __builtin_bit_cast(float, static_cast<unsigned>(x[1]));
+                        }
+                        const float n0 = (b3 ? z[2] : z[0]) + dpp_mov<0x128>(b3 ? z[0] : z[2]);   // row_ror:8 = lane ^ 8
+                        const float n1 = (b3 ? z[3] : z[1]) + dpp_mov<0x128>(b3 ? z[1] : z[3]);
+                        const float send = b2 ? n0 : n1;
+                        const float own = b2 ? n1 : n0;
+                        // row_ror:n moves a value n lanes up its row: lane i reads lane i - n.
+                        const float from_up = dpp_mov<0x12C>(send);     // lane + 4
+                        const float from_dn = dpp_mov<0x124>(send);     // lane - 4
+                        float t = (own + (b2 ? from_dn : from_up)) * a.scale_log2;
+                        if (need_mask && !tok_ok) t = -__builtin_inff();
+                        const float mx = tok_max(t);
+                        const float m_new = __builtin_fmaxf(m_run[r], mx);
+                        const float alpha = fast_exp2(m_run[r] - m_new);
+                        m_run[r] = m_new;
+                        const _Float16 ph = static_cast<_Float16>(fast_exp2(t - m_new));
+                        l_run[r] = __builtin_fmaf(l_run[r], alpha, static_cast<float>(ph));
+                        s_p[wave][r][lp][t_lane] = ph;
+                        pr[r] = alpha;
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    // Rescale the accumulators by each head's factor (one
+                    // value per quarter, read from lanes 0, 4, 8, 12).
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) {
+                        const float f0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), 0));
+                        const float f1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), 4));
+                        const float f2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), 8));
+                        const float f3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[r]), 12));
+                        if (f0 != 1.f || f1 != 1.f || f2 != 1.f || f3 != 1.f) {
+#pragma unroll
+                            for (int n = 0; n < NG; ++n) {
+                                acc[r][n][0] *= f0;
+                                acc[r][n][1] *= f1;
+                                acc[r][n][2] *= f2;
+                                acc[r][n][3] *= f3;
+                            }
+                        }
+                    }
+                    // V rows to the wave's LDS tile, then refill.
+#pragma unroll
+                    for (int v = 0; v < VL; ++v)
+                        *reinterpret_cast<uint4*>(vtile + v_wr_off + RPL * v * VROW) = vd[v];
+                    __builtin_amdgcn_wave_barrier();
+                    issue_v(vd, nxt);
+                    // P.V: k-step ks takes tokens 4ks .. 4ks+3.
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        mf_h4 pa[RS];
+#pragma unroll
+                        for (int r = 0; r < RS; ++r)
+                            pa[r] = *reinterpret_cast<const mf_h4*>(&s_p[wave][r][lj][4 * ks]);
+#pragma unroll
+                        for (int n = 0; n < NG; ++n) {
+                            const mf_s4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_s4*)(vtile + v_rd_off + 4 * ks * VROW + 128 * n));
+                            const mf_h4 vb = __builtin_bit_cast(mf_h4, raw);
+#pragma unroll
+                            for (int r = 0; r < RS; ++r)
+                                acc[r][n] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[r], vb, acc[r][n], 0, 0, 0);
+                        }
+                    }
+                };
+
+                if (nw > 0) {
+                    uint4 xk[KM], xv[VL], yk[KM], yv[VL];
+                    {
+                        const Src r0 = source(0, true);
+                        issue_k(xk, r0);
+                        issue_v(xv, r0);
+                        const Src r1 = source(1, 1 < nw);
+                        issue_k(yk, r1);
+                        issue_v(yv, r1);
+                    }
+                    int k = 0;
+                    for (; k + 1 < nw; k += 2) {
+                        consume(xk, xv, k, k + 2, k + 2 < nw);
+                        consume(yk, yv, k + 1, k + 3, k + 3 < nw);
+                    }
+                    if (k < nw) consume(xk, xv, k, k + 2, false);
+                }
+            }
+
+            // Row sums over the chunk tokens of this wave; then to LDS.
+#pragma unroll
+            for (int r = 0; r < RS; ++r) {
+                const float lw = tok_sum(l_run[r]);
+                const int h = 4 * r + lp;
+                if (ltg == 0 && lj == 0 && h < G) {
+                    s_m[wave][h] = m_run[r];
+                    s_l[wave][h] = lw;
+                }
+#pragma unroll
+                for (int n = 0; n < NG; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * r + i < G) s_acc[wave][4 * r + i][64 * n + lane] = acc[r][n][i];
+            }
+            __syncthreads();
+
+            const bool whole = c0 == 0 && c1 == nch;
+            const size_t slot = static_cast<size_t>(unit) + static_cast<size_t>(s) * Hkv + g;
+            for (int o = threadIdx.x; o < G * D; o += kThreads) {
+                const int h = o / D;
+                const int d = o % D;
+                float mm = s_m[0][h];
+#pragma unroll
+                for (int v = 1; v < kWaves; ++v) mm = __builtin_fmaxf(mm, s_m[v][h]);
+                float num = 0.f, den = 0.f;
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) {
+                    const float f = fast_exp2(s_m[v][h] - mm);
+                    num = __builtin_fmaf(f, s_acc[v][h][d], num);
+                    den = __builtin_fmaf(f, s_l[v][h], den);
+                }
+                if (whole) {
+                    const float r = den == 0.f ? 0.f : num / den;
+                    a.out[out_row0 + o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
+                } else {
+                    a.part_o[(slot * G + h) * D + d] = num;
+                    if (d == 0) {
+                        a.part_ml[(slot * G + h) * 2] = mm;
+                        a.part_ml[(slot * G + h) * 2 + 1] = den;
+                    }
+                }
+            }
+
+            pos += n_seg;
+            if (pos >= end) break;
+            __syncthreads();
+            c0 = 0;
+            if (++g == Hkv) {
+                g = 0;
+                L = 0;
+                while (L == 0 && s + 1 < a.num_seqs) L = len_of(++s);
+                nch = chunks_of(L);
+                if (nch == 0) break;
+            }
+        }
+    };
+
+    const int u = blockIdx.x;
+    int64_t start, end;
+    if (a.whole_pairs) {
+        const int s = u / Hkv;
+        const int g = u - s * Hkv;
+        const int L = __builtin_amdgcn_readlane(len_reg, s);
+        const int nch = chunks_of(L);
+        if (nch == 0) {
+            for (int o = threadIdx.x; o < G * D; o += kThreads)
+                a.out[(static_cast<size_t>(s) * a.num_q_heads + g * G) * D + o] = 0;
+            return;
+        }
+        start = (readlane64(incl_reg, s) - nch) * Hkv + static_cast<int64_t>(g) * nch;
+        end = start + nch;
+    } else {
+        start = static_cast<int64_t>(u) * U / N;
+        end = static_cast<int64_t>(u + 1) * U / N;
+    }
+    if (start < end) process_split(u, start, end);
+}
+
 // Merge the partials of pairs that span several splits, and write the zero
 // rows of empty contexts.  One workgroup of 4 waves per (sequence, KV head)
 // pair; pairs the split kernel wrote whole return at once.
@@ -728,9 +1195,20 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
     }
 }
 
+// Matrix cores take groups of 3 to 8 query heads (block >= 16); the vector
+// kernel takes groups of 1 and 2 and block size 8.
+template <int BS, int G>
+constexpr bool use_mfma() { return BS >= kChunk && G >= 3 && G <= 8; }
+
+template <int D, int BS, int G>
+constexpr auto split_kernel() {
+    if constexpr (use_mfma<BS, G>()) return decode_mfma_kernel<D, BS, G>;
+    else return decode_split_kernel<D, BS, G>;
+}
+
 template <int D, int BS, int G>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, BS, G>), dim3(a.num_splits), dim3(kThreads), 0,
+    hipLaunchKernelGGL((split_kernel<D, BS, G>()), dim3(a.num_splits), dim3(kThreads), 0,
                        stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.whole_pairs) return err;
@@ -750,12 +1228,16 @@ int resident_one() {
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, BS, G>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel<D, BS, G>(),
                                                      kThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
+    // The matrix-core kernel fits 4 workgroups a CU, but 3 stream faster
+    // (measured: 4 x 131072-token contexts 342 vs 370 us a call, mixed lengths
+    // 104 vs 105 us); the vector kernels use what fits.
+    if (use_mfma<BS, G>() && per_cu > 3) per_cu = 3;
     v = per_cu * cus;
     if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
     return v;
