@@ -215,7 +215,19 @@ def parity_summary(diffs, refs):
     return out
 
 
-def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None, layout="slot"):
+def cpu_model():
+    """The host CPU's model name (first ``model name`` line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None, layout="slot", full_pass=False):
     """The fp64 oracle on the host cores: one layer, sequences taken in batch
     order until about ``budget_s`` seconds of work.  With ``out0`` (the GPU's
     output of the same layer) the first pass over the batch is also compared
@@ -224,6 +236,8 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None, layout="slot"):
 
     from oracle import decode_ref
     cores = len(os.sched_getaffinity(0))
+    # The box grants one GPU's share of the host (16 cores) whatever the
+    # affinity mask shows; the oracle's BLAS threads stay within that share.
     threads = min(cores, 16)
     kh = kc0.cpu().numpy()
     vh = vc0.cpu().numpy()
@@ -234,7 +248,7 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None, layout="slot"):
     lens = np.asarray(plan.context_lens, dtype=np.int32)
     done, tokens, nbytes, elapsed = 0, 0, 0, 0.0
     with threadpool_limits(limits=threads):
-        while elapsed < budget_s and done < 64 * len(lens):
+        while (elapsed < budget_s or (full_pass and done < len(lens))) and done < 64 * len(lens):
             s = done % len(lens)
             t0 = time.perf_counter()
             ref = decode_ref(qh[s:s + 1], kh, vh, tables[s:s + 1], lens[s:s + 1], wl.scale,
@@ -249,6 +263,7 @@ def cpu_baseline(wl, plan, kc0, vc0, q0, budget_s, out0=None, layout="slot"):
                                    wl.head_dim, wl.block_size)
     result = {
         "value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "affinity_cores": cores, "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, one layer of the same workload: {done} sequence "
                    f"decodes ({tokens} context tokens, batch order, repeating) in "
@@ -398,6 +413,7 @@ def prefill_cpu_baseline(wl, kc, vc, q, tables, lens, chunk, budget_s, out0=None
     elapsed = time.perf_counter() - t0
     result = {
         "value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle: {done} causal rows (all {wl.num_q_heads} query heads) "
                    f"of one sequence's chunk, one layer, in {elapsed:.2f} s"),
@@ -516,6 +532,246 @@ def prefill_main(args, wl, dev):
     print(json.dumps(result), flush=True)
 
 
+def unique_kv_rows(block_tables, lens, block_size):
+    """Distinct (physical block, row) cache slots the batch attends to."""
+    seen = set()
+    for row, L in zip(block_tables, lens):
+        L = int(L)
+        for p in range(L):
+            seen.add(int(row[p // block_size]) * block_size + p % block_size)
+    return len(seen)
+
+
+def time_decode_only(wl, st, layout, splits, steps, warmup):
+    """pa_decode alone over every layer, ``steps`` times, HIP events around
+    each call; for comparing partitions of the same batch."""
+    import torch
+
+    import paged_kv_cache_382_amd as pa
+    caches, q, out = st["caches"], st["q"], st["out"]
+    desc = st["desc"]
+    B = q.shape[1]
+    ws = pa.decode_workspace(desc, B, q.shape[2], splits, q.device)
+    max_ctx = max(st["lens"])
+
+    def run(ev=None):
+        for layer, (kc, vc) in enumerate(caches):
+            if ev is not None:
+                ev[layer][0].record()
+            pa.pa_decode(q[layer], kc, vc, st["tables"], st["lens_d"], wl.scale, out=out[layer],
+                         max_context_len=max_ctx, num_splits=splits, workspace=ws, layout=layout)
+            if ev is not None:
+                ev[layer][1].record()
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in caches] for _ in range(steps)]
+    for k in range(steps):
+        run(evs[k])
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for row in evs for a, b in row]
+    n_dec = decode_bytes(st["lens"], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size)
+    achieved = n_dec / (float(np.mean(ms)) * 1e-3) / 1e9
+    return {"num_splits": {0: "auto", -1: "whole pairs"}.get(splits, splits),
+            "decode_us_percentiles": pcts([x * 1e3 for x in ms]),
+            "achieved": round(achieved, 2), "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "kernel": decode_kernel_label(splits, B, max_ctx)}
+
+
+def run_decode(wl, dev, layout="slot", splits_arg=0, steps=20, warmup=3, layers=None,
+               do_graph=True, do_ceiling=True, cpu_budget=15.0):
+    """One decode workload: plan with the C++ allocator, build the caches,
+    time ``steps`` steps of every layer (HIP events around each step and each
+    pa_decode call), then the optional graph replay, read ceiling and CPU
+    oracle.  Returns the result dict (the JSON line's fields) and the state
+    the caller may reuse."""
+    import torch
+
+    import paged_kv_cache_382_amd as pa
+    layers = layers or wl.layers
+    alloc = pa.Allocator(wl.num_blocks, wl.block_size, wl.max_blocks_per_seq,
+                         W.free_order(wl.num_blocks, wl.seed))
+    plan = W.plan_for(wl, alloc)
+    stats = alloc.stats()
+    B = len(plan.seq_ids)
+    lens = [int(x) for x in plan.context_lens]
+    max_ctx = max(lens)
+    hkv, hq, d, bs = wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.block_size
+
+    shape = cache_shape(wl, layout)
+    caches = []
+    for layer in range(layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(wl.seed * 100000 + layer)
+        kc = torch.randn(shape, generator=g, device=dev, dtype=torch.float16)
+        vc = torch.randn(shape, generator=g, device=dev, dtype=torch.float16)
+        caches.append((kc, vc))
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    q = torch.randn((layers, B, hq, d), generator=g, device=dev, dtype=torch.float16)
+    k_new = torch.randn((layers, B, hkv, d), generator=g, device=dev, dtype=torch.float16)
+    v_new = torch.randn((layers, B, hkv, d), generator=g, device=dev, dtype=torch.float16)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(np.ascontiguousarray(plan.block_tables, dtype=np.int32)).to(dev)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
+    slots = torch.tensor(list(plan.step_slots), dtype=torch.int32, device=dev)
+    cows = torch.tensor([list(c) for c in plan.cow_pairs], dtype=torch.int32,
+                        device=dev).reshape(-1, 2)
+    desc = pa.cache_desc(caches[0][0], layout)
+    splits = splits_arg                 # 0: the library's choice for this batch
+    if (splits == 0 and B <= 64 and min(lens) == max(lens)
+            and B * hkv >= pa.pa_decode_num_splits(desc, hq, 0)):
+        # The host knows the lengths: all equal, and the pairs alone fill the
+        # device, so the balanced split is one workgroup per (sequence, KV head)
+        # pair and the merge would find nothing; ask for that partition.
+        splits = -1
+    ws = pa.decode_workspace(desc, B, hq, splits, dev)
+
+    def step(events=None):
+        for layer in range(layers):
+            kc, vc = caches[layer]
+            if cows.numel():
+                pa.pa_copy_blocks(kc, vc, cows, layout=layout)
+            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc, layout=layout)
+            if events is not None:
+                events[layer][0].record()
+            pa.pa_decode(q[layer], kc, vc, tables, lens_d, wl.scale, out=out[layer],
+                         max_context_len=max_ctx, num_splits=splits, workspace=ws,
+                         layout=layout)
+            if events is not None:
+                events[layer][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(layers)] for _ in range(steps)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record()
+    for k in range(steps):
+        step(events[k])
+        marks[k + 1].record()
+    torch.cuda.synchronize()
+    step_ms = marks[0].elapsed_time(marks[-1]) / steps
+    step_each = [marks[k].elapsed_time(marks[k + 1]) for k in range(steps)]
+    dec_ms = [e[0].elapsed_time(e[1]) for row in events for e in row]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    graph = None
+    if do_graph:
+        g = pa.DecodeStepGraph(caches, q, k_new, v_new, slots, tables, lens_d, wl.scale, out,
+                               cow_pairs=cows, num_splits=splits,
+                               layout=layout)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(steps):
+            g.replay()
+        ge.record()
+        torch.cuda.synchronize()
+        graph = gs.elapsed_time(ge) / steps
+
+    ceiling = None
+    if do_ceiling:
+        # Caches smaller than 1 GiB would be read from the 256 MB last-level
+        # cache: probe a dedicated 2 GiB buffer instead.
+        big = caches[0][0].numel() * 2 >= 1 << 30
+        probe_bufs = list(caches[0]) if big else [torch.empty(1 << 30, dtype=torch.float16, device=dev)]
+        ceiling = read_ceiling(probe_bufs, 5)
+        ceiling["buffers"] = "layer 0's K and V caches" if big else "a dedicated 2 GiB buffer"
+        del probe_bufs
+
+    n_dec = decode_bytes(lens, hq, hkv, d, bs)
+    n_step = layers * (n_dec + store_bytes(B, hkv, d) + copy_bytes(len(plan.cow_pairs), bs, hkv, d))
+    value = n_step / (step_ms * 1e-3) / 1e9
+    achieved = n_dec / (dec_avg_ms * 1e-3) / 1e9
+    traffic = counter_traffic(counter_stem(wl.name, layout))
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": describe(wl, plan),
+            "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
+            "context_min": min(lens), "context_max": max_ctx, "context_sum": sum(lens),
+            "layers": layers,
+            "num_splits": {0: "auto", -1: "whole pairs (equal contexts)"}.get(splits, splits),
+            "pool_blocks": wl.num_blocks,
+            "cache_layout": LAYOUT_NAMES[layout],
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "decode_tokens_per_s": round(B / (step_ms * 1e-3), 2),
+        "decode_us_per_layer": round(dec_avg_ms * 1e3, 3),
+        "step_ms_percentiles": pcts(step_each),
+        "decode_us_percentiles": pcts([x * 1e3 for x in dec_ms]),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": decode_kernel_label(splits, B, max_ctx),
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": n_dec,
+            "flops_per_launch": decode_flops(lens, hq, d),
+        },
+        "allocator": {"utilisation": round(float(stats["utilisation"]), 4),
+                      "internal_fragmentation": round(float(stats["internal_fragmentation"]), 5),
+                      "shared_blocks": int(stats["shared_blocks"]),
+                      "cow_pairs_this_step": len(plan.cow_pairs)},
+        "host_step_us": host_step_cost(wl),
+    }
+    if traffic is not None:
+        result["roofline"]["traffic_over_algorithmic"] = round(traffic / n_dec, 4)
+    lds = counter_lds_conflicts(counter_stem(wl.name, layout))
+    if lds is not None:
+        result["roofline"]["lds_bank_conflict_share"] = lds
+    if ceiling is not None:
+        result["read_ceiling"] = ceiling
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
+    if graph is not None:
+        result["graph"] = {"ms_per_step": round(graph, 4),
+                           "value": round(n_step / (graph * 1e-3) / 1e9, 2),
+                           "decode_tokens_per_s": round(B / (graph * 1e-3), 2)}
+    if cpu_budget != 0:
+        # cpu_budget < 0: one pass over the batch only (every sequence's rows
+        # compared with the oracle), no timing budget beyond it.
+        result["cpu_baseline"] = cpu_baseline(wl, plan, caches[0][0], caches[0][1], q[0],
+                                              max(cpu_budget, 0.0), out0=out[0], layout=layout,
+                                              full_pass=True)
+    if wl.name == "prefix":
+        # Shared prefix blocks are read by every sequence but stored once:
+        # report the bytes the method names (every attended row, "logical")
+        # beside the bytes of distinct cache rows ("unique") and a rate for each.
+        uniq = unique_kv_rows(plan.block_tables, lens, bs)
+        n_unique = (uniq * hkv * d * 2 * 2 + 2 * B * hq * d * 2
+                    + sum(-(-L // bs) for L in lens) * 4 + 4 * B)
+        result["prefix_bytes"] = {
+            "logical_bytes_per_launch": n_dec, "unique_bytes_per_launch": n_unique,
+            "logical_gbps": round(achieved, 2),
+            "unique_gbps": round(n_unique / (dec_avg_ms * 1e-3) / 1e9, 2),
+            "distinct_rows": int(uniq), "attended_rows": int(sum(lens)),
+            "note": "logical: every attended K/V row counted once per sequence (the method's bytes); "
+                    "unique: each distinct cache row counted once (the shared blocks are re-read "
+                    "from the last-level cache)"}
+    return result, {"caches": caches, "q": q, "out": out, "tables": tables, "lens_d": lens_d,
+                    "lens": lens, "plan": plan, "splits": splits, "ws": ws, "desc": desc}
+
 # Longest context for which the library's automatic choice (num_splits 0) runs
 # one workgroup per (sequence, KV head) pair, for batches of at most 64.
 WHOLE_PAIR_MAX_TOKENS = 512
@@ -545,6 +801,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read probe on layer 0's caches")
+    ap.add_argument("--no-mix", dest="with_mix", action="store_false",
+                    help="with the default mha workload, skip the second measured configuration "
+                         "(mixed context lengths, reported under 'mix')")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip timing the step captured as one HIP graph (reported under 'graph')")
     ap.add_argument("--copy-probe", action="store_true",
@@ -578,166 +837,26 @@ def main():
         compaction_probe(wl, dev, max(args.steps, 1))
         return
 
-    alloc = pa.Allocator(wl.num_blocks, wl.block_size, wl.max_blocks_per_seq,
-                         W.free_order(wl.num_blocks, wl.seed))
-    plan = W.plan_for(wl, alloc)
-    stats = alloc.stats()
-    B = len(plan.seq_ids)
-    lens = [int(x) for x in plan.context_lens]
-    max_ctx = max(lens)
-    hkv, hq, d, bs = wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.block_size
-
-    shape = cache_shape(wl, args.layout)
-    caches = []
-    for layer in range(layers):
-        g = torch.Generator(device=dev)
-        g.manual_seed(wl.seed * 100000 + layer)
-        kc = torch.randn(shape, generator=g, device=dev, dtype=torch.float16)
-        vc = torch.randn(shape, generator=g, device=dev, dtype=torch.float16)
-        caches.append((kc, vc))
-    g = torch.Generator(device=dev)
-    g.manual_seed(wl.seed)
-    q = torch.randn((layers, B, hq, d), generator=g, device=dev, dtype=torch.float16)
-    k_new = torch.randn((layers, B, hkv, d), generator=g, device=dev, dtype=torch.float16)
-    v_new = torch.randn((layers, B, hkv, d), generator=g, device=dev, dtype=torch.float16)
-    out = torch.empty_like(q)
-    tables = torch.from_numpy(np.ascontiguousarray(plan.block_tables, dtype=np.int32)).to(dev)
-    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
-    slots = torch.tensor(list(plan.step_slots), dtype=torch.int32, device=dev)
-    cows = torch.tensor([list(c) for c in plan.cow_pairs], dtype=torch.int32,
-                        device=dev).reshape(-1, 2)
-    desc = pa.cache_desc(caches[0][0], args.layout)
-    splits = args.splits                 # 0: the library's choice for this batch
-    if (splits == 0 and B <= 64 and min(lens) == max(lens)
-            and B * hkv >= pa.pa_decode_num_splits(desc, hq, 0)):
-        # The host knows the lengths: all equal, and the pairs alone fill the
-        # device, so the balanced split is one workgroup per (sequence, KV head)
-        # pair and the merge would find nothing; ask for that partition.
-        splits = -1
-    ws = pa.decode_workspace(desc, B, hq, splits, dev)
-
-    def step(events=None):
-        for layer in range(layers):
-            kc, vc = caches[layer]
-            if cows.numel():
-                pa.pa_copy_blocks(kc, vc, cows, layout=args.layout)
-            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc, layout=args.layout)
-            if events is not None:
-                events[layer][0].record()
-            pa.pa_decode(q[layer], kc, vc, tables, lens_d, wl.scale, out=out[layer],
-                         max_context_len=max_ctx, num_splits=splits, workspace=ws,
-                         layout=args.layout)
-            if events is not None:
-                events[layer][1].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in range(layers)] for _ in range(args.steps)]
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    marks[0].record()
-    for k in range(args.steps):
-        step(events[k])
-        marks[k + 1].record()
-    torch.cuda.synchronize()
-    step_ms = marks[0].elapsed_time(marks[-1]) / args.steps
-    step_each = [marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)]
-    dec_ms = [e[0].elapsed_time(e[1]) for row in events for e in row]
-    dec_avg_ms = float(np.mean(dec_ms))
-
-    graph = None
-    if args.graph:
-        g = pa.DecodeStepGraph(caches, q, k_new, v_new, slots, tables, lens_d, wl.scale, out,
-                               cow_pairs=cows, max_context_len=max_ctx, num_splits=splits,
-                               layout=args.layout)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        gs.record()
-        for _ in range(args.steps):
-            g.replay()
-        ge.record()
-        torch.cuda.synchronize()
-        graph = gs.elapsed_time(ge) / args.steps
-
-    ceiling = None
-    if not args.no_read_ceiling:
-        # Caches smaller than 1 GiB would be read from the 256 MB last-level
-        # cache: probe a dedicated 2 GiB buffer instead.
-        big = caches[0][0].numel() * 2 >= 1 << 30
-        probe_bufs = list(caches[0]) if big else [torch.empty(1 << 30, dtype=torch.float16, device=dev)]
-        ceiling = read_ceiling(probe_bufs, 5)
-        ceiling["buffers"] = "layer 0's K and V caches" if big else "a dedicated 2 GiB buffer"
-        del probe_bufs
-
-    n_dec = decode_bytes(lens, hq, hkv, d, bs)
-    n_step = layers * (n_dec + store_bytes(B, hkv, d) + copy_bytes(len(plan.cow_pairs), bs, hkv, d))
-    value = n_step / (step_ms * 1e-3) / 1e9
-    achieved = n_dec / (dec_avg_ms * 1e-3) / 1e9
-    traffic = counter_traffic(counter_stem(wl.name, args.layout))
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {
-            "workload": describe(wl, plan),
-            "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
-            "context_min": min(lens), "context_max": max_ctx, "context_sum": sum(lens),
-            "layers": layers,
-            "num_splits": {0: "auto", -1: "whole pairs (equal contexts)"}.get(splits, splits),
-            "pool_blocks": wl.num_blocks,
-            "cache_layout": LAYOUT_NAMES[args.layout],
-            "parallelism": "single GPU",
-        },
-        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
-        "decode_tokens_per_s": round(B / (step_ms * 1e-3), 2),
-        "decode_us_per_layer": round(dec_avg_ms * 1e3, 3),
-        "step_ms_percentiles": pcts(step_each),
-        "decode_us_percentiles": pcts([x * 1e3 for x in dec_ms]),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": decode_kernel_label(splits, B, max_ctx),
-            "achieved": round(achieved, 2),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": n_dec,
-            "flops_per_launch": decode_flops(lens, hq, d),
-        },
-        "allocator": {"utilisation": round(float(stats["utilisation"]), 4),
-                      "internal_fragmentation": round(float(stats["internal_fragmentation"]), 5),
-                      "shared_blocks": int(stats["shared_blocks"]),
-                      "cow_pairs_this_step": len(plan.cow_pairs)},
-        "host_step_us": host_step_cost(wl),
-    }
-    if traffic is not None:
-        result["roofline"]["traffic_over_algorithmic"] = round(traffic / n_dec, 4)
-    lds = counter_lds_conflicts(counter_stem(wl.name, args.layout))
-    if lds is not None:
-        result["roofline"]["lds_bank_conflict_share"] = lds
-    if ceiling is not None:
-        result["read_ceiling"] = ceiling
-        result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
-    if graph is not None:
-        result["graph"] = {"ms_per_step": round(graph, 4),
-                           "value": round(n_step / (graph * 1e-3) / 1e9, 2),
-                           "decode_tokens_per_s": round(B / (graph * 1e-3), 2)}
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, plan, caches[0][0], caches[0][1], q[0],
-                                              args.cpu_budget, out0=out[0], layout=args.layout)
+    result, st = run_decode(wl, dev, args.layout, args.splits, args.steps, args.warmup, layers,
+                            args.graph, not args.no_read_ceiling,
+                            0.0 if args.no_cpu_baseline else args.cpu_budget)
+    if wl.name == "mha" and st["splits"] == -1 and args.splits == 0:
+        # The headline asks for one workgroup per pair (all contexts equal);
+        # report the library's own choice for the same batch beside it.
+        result["library_default_partition"] = time_decode_only(
+            wl, st, args.layout, 0, max(args.steps // 2, 5), args.warmup)
+    if wl.name == "mha" and args.with_mix:
+        # The second configuration the target names: mixed context lengths.
+        del st
+        torch.cuda.empty_cache()
+        mix_res, mst = run_decode(W.MIX, dev, args.layout, 0, args.steps, args.warmup, None,
+                                  False, False, 0.0 if args.no_cpu_baseline else -1.0)
+        keep = ["config", "ms_per_step", "value", "pct_of_peak", "decode_tokens_per_s",
+                "decode_us_per_layer", "decode_us_percentiles", "roofline", "allocator",
+                "cpu_baseline"]
+        result["mix"] = {k: mix_res[k] for k in keep if k in mix_res}
+        del mst
+        torch.cuda.empty_cache()
     print(json.dumps(result, default=lambda o: o.item() if hasattr(o, "item") else str(o)),
           flush=True)
 

@@ -188,9 +188,13 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  *                  Its contents on entry do not matter; calls sharing a
  *                  workspace must not overlap.
  *
- * Supported: head_dim 64 or 128; block_size 8, 16, 32 or 64; num_q_heads a
- * multiple of num_kv_heads with a group size of 1, 2, 4 or 8.  Other shapes
- * return PA_ERR_UNSUPPORTED.  Results depend only on the context lengths and
+ * Supported: head_dim 64 or 128; block_size 8, 16, 32 or 64; num_q_heads any
+ * multiple of num_kv_heads.  A group G = num_q_heads / num_kv_heads of up to 8
+ * query heads shares each K/V read (groups of 3 to 8 on matrix cores when
+ * block_size >= 16); a larger group runs as G / g groups of its largest
+ * divisor g <= 8, each reading its KV head's rows again (the workspace and
+ * the split count then cover num_kv_heads * G / g pairs per sequence).  Other
+ * shapes return PA_ERR_UNSUPPORTED.  Results depend only on the context lengths and
  * N, never on which physical blocks hold the tokens or on which workgroup
  * handled which range: moving blocks (and rewriting the tables to match)
  * gives bitwise identical output.

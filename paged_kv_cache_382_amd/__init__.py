@@ -229,6 +229,30 @@ def decode_workspace(desc, num_seqs, num_q_heads, num_splits=0, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+def _check_rows(q, out, desc, name):
+    """q (and out, when given) must be [rows, Hq, head_dim] of one shape and dtype."""
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError(f"{name} must be [rows, num_q_heads, {desc.head_dim}] (got {tuple(q.shape)})")
+    if q.shape[1] % desc.num_kv_heads != 0:
+        raise ValueError(f"num_q_heads ({q.shape[1]}) must be a multiple of num_kv_heads "
+                         f"({desc.num_kv_heads})")
+    if out is not None and (tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype):
+        raise ValueError(f"out must match {name} in shape and dtype (got {tuple(out.shape)}, {out.dtype})")
+
+
+def _check_decode_shapes(q, k_cache, v_cache, desc, block_tables, context_lens, out):
+    """Every size the kernels take from the tensors, checked before any launch:
+    the C ABI sees raw pointers, so a mismatched tensor would be read or
+    written past its end."""
+    _check_rows(q, out, desc, "q")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache must have k_cache's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0]:
+        raise ValueError("block_tables must be [B, M] with B = q.shape[0]")
+    if context_lens.numel() != q.shape[0]:
+        raise ValueError("context_lens must be [B]")
+
+
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
               max_context_len=None, num_splits=0, workspace=None, stream=None, layout="slot"):
     """Single-query paged attention; returns ``out`` [B, Hq, D] fp16.
@@ -241,14 +265,13 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
     """
     import torch
     desc = cache_desc(k_cache, layout)
+    _check_decode_shapes(q, k_cache, v_cache, desc, block_tables, context_lens, out)
     B, hq, d = q.shape
     M = block_tables.shape[1]
     if max_context_len is None:
         max_context_len = M * desc.block_size
     if out is None:
         out = torch.empty_like(q)
-    if tuple(block_tables.shape[:1]) != (B,) or context_lens.numel() != B:
-        raise ValueError("block_tables must be [B, M] and context_lens [B]")
     need = pa_decode_workspace_bytes(desc, B, hq, num_splits) if B else 0
     if need and workspace is None:
         workspace = decode_workspace(desc, B, hq, num_splits, q.device)
@@ -277,6 +300,11 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, sca
     """
     import torch
     desc = cache_desc(k_cache, layout)
+    _check_rows(q, out, desc, "q")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache must have k_cache's shape")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, M]")
     T, hq, d = q.shape
     B, M = block_tables.shape
     if context_lens.numel() != B or query_start.numel() != B + 1:
@@ -312,7 +340,10 @@ class DecodeStepGraph:
     single graph launch, without per-kernel launch cost.  As with any graph,
     the tensors are fixed: update their contents in place between replays
     (new rows, slots, tables, lengths, queries); shapes and the number of
-    copy pairs cannot change.
+    copy pairs cannot change.  The decode is captured with the table bound
+    (max_blocks_per_seq * block_size) as its length bound, so lengths can grow
+    in place up to what the tables hold; an explicit smaller
+    ``max_context_len`` is refused.
 
     layers: list of (k_cache, v_cache); q, k_new, v_new, out: per-layer lists
     of tensors (q/out [B, Hq, D], k_new/v_new [N, Hkv, D]); the metadata is
@@ -325,10 +356,18 @@ class DecodeStepGraph:
         self.layers = list(layers)
         self.args = (q, k_new, v_new, slot_mapping, block_tables, context_lens, out, cow_pairs)
         self.scale = float(scale)
-        self.max_context_len = max_context_len
         self.layout = layout
         kc0 = self.layers[0][0]
         desc = cache_desc(kc0, layout)
+        # The bound is fixed at capture and lengths may grow between replays:
+        # capture with the largest length the tables can hold, so that no
+        # context is ever clamped.
+        bound = block_tables.shape[1] * desc.block_size
+        if max_context_len is not None and int(max_context_len) < bound:
+            raise ValueError(f"max_context_len {max_context_len} is below the table bound {bound} "
+                             "(max_blocks_per_seq * block_size); contexts that grow past it would be "
+                             "clamped in replays")
+        self.max_context_len = bound
         B, hq = q[0].shape[0], q[0].shape[1]
         self.num_splits = int(num_splits)
         self.workspace = decode_workspace(desc, B, hq, self.num_splits, kc0.device)

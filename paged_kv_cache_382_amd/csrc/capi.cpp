@@ -63,8 +63,13 @@ pa_status fetch(const int32_t* dev, size_t n, std::vector<int32_t>& host, hipStr
     return PA_OK;
 }
 
+// Query heads per kernel group and virtual KV heads per KV head.
+GroupSplit group_split(const pa_cache_desc* c, int32_t num_q_heads) {
+    return decode_group_split(num_q_heads / c->num_kv_heads);
+}
+
 int32_t resident_workgroups(const pa_cache_desc* c, int32_t num_q_heads) {
-    const int r = decode_resident_workgroups(c->head_dim, c->block_size, num_q_heads / c->num_kv_heads);
+    const int r = decode_resident_workgroups(c->head_dim, c->block_size, group_split(c, num_q_heads).group);
     return r > 0 ? r : kFallbackResident;
 }
 
@@ -87,10 +92,13 @@ constexpr int32_t kWholePairs = -1;
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Partial-result slots: one per split plus one per (sequence, KV head).
+// Partial-result slots: one per split plus one per (sequence, KV head) pair
+// (virtual KV heads for a large query group), each of `group` rows.
 size_t partial_rows(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads, int32_t splits) {
-    const size_t slots = static_cast<size_t>(splits) + static_cast<size_t>(num_seqs) * c->num_kv_heads;
-    return slots * static_cast<size_t>(num_q_heads / c->num_kv_heads);
+    const GroupSplit gs = group_split(c, num_q_heads);
+    const size_t slots = static_cast<size_t>(splits) +
+                         static_cast<size_t>(num_seqs) * c->num_kv_heads * gs.kv_split;
+    return slots * static_cast<size_t>(gs.group);
 }
 
 // Workspace layout: part_ml fp32 [slots][G][2], then part_o fp32
@@ -109,7 +117,7 @@ pa_status check_decode_shapes(const pa_cache_desc* c, int32_t num_seqs, int32_t 
     if (num_q_heads % c->num_kv_heads != 0)
         return fail(PA_ERR_SHAPE, "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
                     num_q_heads, c->num_kv_heads);
-    if (!decode_supported(c->head_dim, c->block_size, num_q_heads / c->num_kv_heads))
+    if (!decode_supported(c->head_dim, c->block_size, group_split(c, num_q_heads).group))
         return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d, block_size %d, group %d not supported", fn,
                     c->head_dim, c->block_size, num_q_heads / c->num_kv_heads);
     if (num_splits < kWholePairs || num_splits > kMaxSplits)
@@ -262,6 +270,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
         if (num_splits == 0) {
             // No more splits than chunks can exist: small batches launch a small grid.
             const int64_t chunk_bound = static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
+                                        pa::group_split(cache, num_q_heads).kv_split *
                                         ((max_tokens64 + 15) / 16);
             splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, chunk_bound)));
         }
@@ -271,7 +280,8 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
             return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
         if (reinterpret_cast<uintptr_t>(workspace) % pa::kAlign != 0)
             return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-        const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads;
+        const pa::GroupSplit gsplit = pa::group_split(cache, num_q_heads);
+        const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads * gsplit.kv_split;
         if (pairs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld pairs)", fn, (long long)pairs);
         hipStream_t stream = static_cast<hipStream_t>(hip_stream);
         if (pa::validate_flag()) {
@@ -317,6 +327,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
         a.num_splits = splits;
         a.scale_log2 = scale * pa::kLog2e;
         a.head_major = cache->layout == PA_LAYOUT_HEAD_MAJOR;
+        a.kv_split = gsplit.kv_split;
         a.whole_pairs = 0;
         if (num_splits == pa::kWholePairs && num_seqs > 64)
             return fail(PA_ERR_RANGE, "%s: num_splits -1 (whole pairs) takes at most 64 sequences", fn);

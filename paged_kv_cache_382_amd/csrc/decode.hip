@@ -200,13 +200,15 @@ void decode_split_kernel(const DecodeArgs a) {
     const int wave = uniform(threadIdx.x / kWave);
     const int row = lane / LPR;
     const int col = lane % LPR;
-    const int Hkv = a.num_kv_heads;
+    // (sequence, KV head) pairs per sequence: virtual heads when a large
+    // query group is cut into several (each re-reads its KV head's rows).
+    const int Hkv = a.num_kv_heads * a.kv_split;
     const int N = a.num_splits;
 
     // Bytes from one token's row of a KV head to the next token's: a whole slot
     // (slot-major) or one head row (head-major).
-    const uint32_t row_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(Hkv) * D * 2;
-    const uint32_t block_bytes = static_cast<uint32_t>(Hkv) * D * 2 * BS;
+    const uint32_t row_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+    const uint32_t block_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2 * BS;
     // Per-lane byte offset inside a load: row `row` of the load, 16-byte column `col`.
     const uint32_t lane_off = row * row_bytes + col * 16;
 
@@ -278,7 +280,7 @@ void decode_split_kernel(const DecodeArgs a) {
             const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
             const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
             // KV head g's first row in a block.
-            const size_t head_off = static_cast<size_t>(g) * D * 2 * (a.head_major ? BS : 1);
+            const size_t head_off = static_cast<size_t>(g / a.kv_split) * D * 2 * (a.head_major ? BS : 1);
             const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
             const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
 
@@ -702,11 +704,13 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int lj = lane & 3;                      // token in group (B, D) / query row (A)
     const int lp = (lane >> 2) & 3;               // quarter of the head dimension / head after the sum
     const int ltg = lane >> 4;                    // token group
-    const int Hkv = a.num_kv_heads;
+    // (sequence, KV head) pairs per sequence: virtual heads when a large
+    // query group is cut into several (each re-reads its KV head's rows).
+    const int Hkv = a.num_kv_heads * a.kv_split;
     const int N = a.num_splits;
 
-    const uint32_t row_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(Hkv) * D * 2;
-    const uint32_t block_bytes = static_cast<uint32_t>(Hkv) * D * 2 * BS;
+    const uint32_t row_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+    const uint32_t block_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2 * BS;
     // K loads: lane 4*b + j reads slice b % SL of row j + 4*(b / SL) of the
     // load's TPL rows -- whole rows per instruction, in the lane order of the
     // B operand (block b = slice, column j = row).
@@ -774,7 +778,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
             const int h0 = g * G;
             const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
             const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
-            const size_t head_off = static_cast<size_t>(g) * D * 2 * (a.head_major ? BS : 1);
+            const size_t head_off = static_cast<size_t>(g / a.kv_split) * D * 2 * (a.head_major ? BS : 1);
             const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
             const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
 
@@ -1087,7 +1091,9 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
     static_assert(kO % 4 == 0, "pieces of 4 outputs");
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int Hkv = a.num_kv_heads;
+    // (sequence, KV head) pairs per sequence: virtual heads when a large
+    // query group is cut into several (each re-reads its KV head's rows).
+    const int Hkv = a.num_kv_heads * a.kv_split;
     const int N = a.num_splits;
     const int s = blockIdx.x / Hkv;
     const int g = blockIdx.x % Hkv;
@@ -1212,7 +1218,7 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
                        stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.whole_pairs) return err;
-    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.num_seqs * a.num_kv_heads), dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.num_seqs * a.num_kv_heads * a.kv_split), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -1248,7 +1254,11 @@ int resident_group(int group) {
     switch (group) {
         case 1: return resident_one<D, BS, 1>();
         case 2: return resident_one<D, BS, 2>();
+        case 3: return resident_one<D, BS, 3>();
         case 4: return resident_one<D, BS, 4>();
+        case 5: return resident_one<D, BS, 5>();
+        case 6: return resident_one<D, BS, 6>();
+        case 7: return resident_one<D, BS, 7>();
         case 8: return resident_one<D, BS, 8>();
         default: return 0;
     }
@@ -1267,10 +1277,14 @@ int resident_block(int block_size, int group) {
 
 template <int D, int BS>
 hipError_t dispatch_group(const DecodeArgs& a, hipStream_t stream) {
-    switch (a.num_q_heads / a.num_kv_heads) {
+    switch (a.num_q_heads / (a.num_kv_heads * a.kv_split)) {
         case 1: return launch_one<D, BS, 1>(a, stream);
         case 2: return launch_one<D, BS, 2>(a, stream);
+        case 3: return launch_one<D, BS, 3>(a, stream);
         case 4: return launch_one<D, BS, 4>(a, stream);
+        case 5: return launch_one<D, BS, 5>(a, stream);
+        case 6: return launch_one<D, BS, 6>(a, stream);
+        case 7: return launch_one<D, BS, 7>(a, stream);
         case 8: return launch_one<D, BS, 8>(a, stream);
         default: return hipErrorInvalidValue;
     }
@@ -1289,10 +1303,19 @@ hipError_t dispatch_block(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+GroupSplit decode_group_split(int group) {
+    // Groups of up to 8 query heads run as they are; a larger group is cut
+    // into kv_split equal groups of its largest divisor not above 8.
+    if (group <= 8) return {group, 1};
+    int g = 8;
+    while (group % g != 0) --g;
+    return {g, group / g};
+}
+
 bool decode_supported(int head_dim, int block_size, int group) {
     const bool d_ok = head_dim == 64 || head_dim == 128;
     const bool b_ok = block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
-    const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
+    const bool g_ok = group >= 1 && group <= 8;      // larger groups are cut into these
     return d_ok && b_ok && g_ok;
 }
 

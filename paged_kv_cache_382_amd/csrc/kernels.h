@@ -31,8 +31,19 @@ struct DecodeArgs {
     int32_t whole_pairs;           // 1: workgroup w takes (sequence, KV head) pair w whole
                                    // (N = num_seqs * num_kv_heads, at most 64 sequences, no merge)
     int32_t head_major;            // 1: cache [NB][Hkv][BS][D], else [NB][BS][Hkv][D]
+    int32_t kv_split;              // virtual KV heads per KV head (>= 1): a query group of
+                                   // G > 8 heads runs as kv_split groups of G / kv_split
 };
 
+// The query group a decode kernel takes (at most 8 heads) and how many such
+// groups each KV head's group is cut into.
+struct GroupSplit {
+    int group;
+    int kv_split;
+};
+GroupSplit decode_group_split(int group);
+
+// group: heads per kernel group (1..8, after decode_group_split).
 bool decode_supported(int head_dim, int block_size, int group);
 // Workgroups of the decode kernel for these shapes that the current device
 // holds at once; 0 when no device can be queried.

@@ -80,7 +80,7 @@ def test_graph_replays_equal_eager_step(layout):
     out_graph = torch.full_like(q, float("nan"))
     step = pa.DecodeStepGraph(graph_caches, q, k_new, v_new, meta["slots"], meta["tables"],
                               meta["lens"], WL.scale, out_graph, cow_pairs=meta["cows"],
-                              max_context_len=meta["max_ctx"], layout=layout)
+                              layout=layout)
     other = torch.empty_like(q[0])
     for rep in range(3):
         out_graph.fill_(float("nan"))
@@ -97,3 +97,61 @@ def test_graph_replays_equal_eager_step(layout):
                      WL.scale, out=other, max_context_len=meta["max_ctx"], layout=layout)
         _ = (other.float() * 2).sum().item()
         torch.cuda.synchronize()
+
+
+def test_graph_replays_while_contexts_grow():
+    """Lengths grow in place between replays, past the longest context at
+    capture time: the captured decode must not clamp them (it is captured
+    with the table bound), and every replay equals the eager step."""
+    wl = W.shrink(W.MIX, name="graph_grow", num_seqs=5, num_blocks=512, max_blocks_per_seq=32,
+                  num_q_heads=8, num_kv_heads=2)
+    lens0 = [3, 40, 97, 130, 200]
+    order = W.free_order(wl.num_blocks, wl.seed)
+    alloc = pa.Allocator(wl.num_blocks, wl.block_size, wl.max_blocks_per_seq, order)
+    plan = W._plain_plan(alloc, wl, lens0)
+    B = len(plan.seq_ids)
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    layers = [(W.normal_fp16(shape, 40 + 2 * i, DEV), W.normal_fp16(shape, 41 + 2 * i, DEV))
+              for i in range(2)]
+    q = W.normal_fp16((2, B, wl.num_q_heads, wl.head_dim), 50, DEV)
+    k_new = W.normal_fp16((2, B, wl.num_kv_heads, wl.head_dim), 51, DEV)
+    v_new = W.normal_fp16((2, B, wl.num_kv_heads, wl.head_dim), 52, DEV)
+    slots = torch.tensor(list(plan.step_slots), dtype=torch.int32, device=DEV)
+    tables = torch.from_numpy(np.ascontiguousarray(plan.block_tables, dtype=np.int32)).to(DEV)
+    lens = torch.tensor(list(plan.context_lens), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        pa.DecodeStepGraph(layers, q, k_new, v_new, slots, tables, lens, wl.scale,
+                           torch.empty_like(q), max_context_len=max(plan.context_lens))
+    out_graph = torch.empty_like(q)
+    out_eager = torch.empty_like(q)
+    say("graph grow: capture")
+    step = pa.DecodeStepGraph(layers, q, k_new, v_new, slots, tables, lens, wl.scale, out_graph)
+    torch.cuda.synchronize()
+    # the eager side starts from the caches as capture left them (capture runs
+    # one step eagerly first)
+    eager_layers = [(kc.clone(), vc.clone()) for kc, vc in layers]
+    for it in range(60):
+        # the step's rows: each sequence gains one token
+        new_slots, cows = alloc.append_batch(plan.seq_ids)
+        assert len(cows) == 0
+        t_host, l_host = alloc.export(plan.seq_ids, wl.max_blocks_per_seq)
+        slots.copy_(torch.from_numpy(np.ascontiguousarray(new_slots, dtype=np.int32)))
+        tables.copy_(torch.from_numpy(np.ascontiguousarray(t_host, dtype=np.int32)))
+        lens.copy_(torch.from_numpy(np.ascontiguousarray(l_host, dtype=np.int32)))
+        k_new.copy_(W.normal_fp16(k_new.shape, 1000 + it, DEV))
+        v_new.copy_(W.normal_fp16(v_new.shape, 2000 + it, DEV))
+        q.copy_(W.normal_fp16(q.shape, 3000 + it, DEV))
+        if it % 20 == 19:
+            say(f"graph grow: replay {it} (longest context {int(max(l_host))})")
+        step.replay()
+        for layer, (kc, vc) in enumerate(eager_layers):
+            pa.pa_store_kvcache(k_new[layer], v_new[layer], slots, kc, vc)
+            pa.pa_decode(q[layer], kc, vc, tables, lens, wl.scale, out=out_eager[layer])
+        torch.cuda.synchronize()
+        assert torch.equal(out_graph.view(torch.int16), out_eager.view(torch.int16)), f"step {it}"
+    assert int(max(l_host)) > max(plan.context_lens) + 50
+    # the last step against the oracle (layer 1)
+    ref = decode_ref(host_u16(q[1]).view(np.float16), host_u16(eager_layers[1][0]).view(np.float16),
+                     host_u16(eager_layers[1][1]).view(np.float16), np.asarray(t_host),
+                     np.asarray(l_host), wl.scale)
+    check_close(out_graph[1], ref, "graph grow: last replay")
