@@ -207,6 +207,27 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* out, int32_t num_splits,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The partial results live in a file-scope device
+ * array of 8 MiB (8388608 bytes) that every GPU the library runs on holds
+ * until the process ends; the call allocates
+ * nothing (no hipMalloc, no host allocation) and does not apply validation
+ * mode.  Arguments, layouts and results as pa_decode (same kernels, bitwise
+ * the same output for the same num_splits).
+ *
+ * Errors: PA_ERR_WORKSPACE, before any launch, when the call's partial
+ * results need more than the scratch holds (workspace formula as
+ * pa_decode_workspace_bytes); the other errors of pa_decode.
+ * Every call on one GPU shares that GPU's scratch and keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller. */
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const pa_cache_desc* cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, void* out, int32_t num_splits, void* hip_stream);
+
 /* Bytes of workspace pa_decode needs: (N + num_seqs * num_kv_heads) slots of
  * G x (head_dim + 2) floats, with G = num_q_heads / num_kv_heads and N the
  * resolved num_splits, each of the two arrays rounded up to 256 bytes.

@@ -17,7 +17,7 @@ import numpy as np
 
 __all__ = [
     "PaError", "CacheDesc", "lib",
-    "pa_store_kvcache", "pa_copy_blocks", "pa_decode", "pa_prefill",
+    "pa_store_kvcache", "pa_copy_blocks", "pa_decode", "pa_decode_noalloc", "pa_prefill",
     "pa_decode_workspace_bytes", "pa_decode_num_splits",
     "pa_set_validate", "pa_version", "Allocator", "decode_workspace", "DecodeStepGraph",
 ]
@@ -74,6 +74,8 @@ SIGNATURES = {
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P]),
     "pa_decode": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P, _I32, _I32,
                                  _I32, ctypes.c_float, _P, _I32, _P, ctypes.c_size_t, _P]),
+    "pa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P, _I32,
+                                         _I32, _I32, ctypes.c_float, _P, _I32, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32]),
     "pa_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "pa_decode_num_splits": (_I32, [ctypes.POINTER(CacheDesc), _I32, _I32]),
@@ -284,6 +286,33 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         _dev(context_lens, torch.int32, "context_lens"), B, hq, int(max_context_len),
         float(scale), _dev(out, torch.float16, "out"), int(num_splits), ws_ptr, ws_bytes,
         _stream(stream)))
+    return out
+
+
+# Bytes of the device array that pa_decode_noalloc keeps its partial results in.
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                      max_context_len=None, num_splits=0, stream=None, layout="slot"):
+    """pa_decode with the partial results in the library's own device array
+    (no workspace, no allocation); ``out`` must be given.  Calls that overlap
+    on one GPU share that array and must be serialised by the caller."""
+    import torch
+    desc = cache_desc(k_cache, layout)
+    if out is None:
+        raise ValueError("pa_decode_noalloc writes into a caller-provided out")
+    _check_decode_shapes(q, k_cache, v_cache, desc, block_tables, context_lens, out)
+    B, hq, d = q.shape
+    M = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = M * desc.block_size
+    _check(lib().pa_decode_noalloc(
+        _dev(q, torch.float16, "q"), _dev(k_cache, torch.float16, "k_cache"),
+        _dev(v_cache, torch.float16, "v_cache"), ctypes.byref(desc),
+        _dev(block_tables, torch.int32, "block_tables"), M,
+        _dev(context_lens, torch.int32, "context_lens"), B, hq, int(max_context_len),
+        float(scale), _dev(out, torch.float16, "out"), int(num_splits), _stream(stream)))
     return out
 
 

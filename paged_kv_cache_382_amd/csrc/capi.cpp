@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -123,6 +124,155 @@ pa_status check_decode_shapes(const pa_cache_desc* c, int32_t num_seqs, int32_t 
     if (num_splits < kWholePairs || num_splits > kMaxSplits)
         return fail(PA_ERR_RANGE, "%s: num_splits must be in [-1, %d]", fn, kMaxSplits);
     return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+namespace pa {
+namespace {
+
+// Device memory of pa_decode_noalloc's partial results: a file-scope array of
+// kScratchBytes on every GPU the library runs on, held until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// is a stand-in, not device memory): the device address of each GPU's copy is
+// looked up once per device with hipGetSymbolAddress and kept here.
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex& scratch_mutex() {
+    static std::mutex m;
+    return m;
+}
+void* scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's scratch address (looked up on its first use).
+pa_status scratch_for_current_device(void** out, const char* fn) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(err));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(PA_ERR_RANGE, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(scratch_mutex());
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !p)
+            return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(err));
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return PA_OK;
+}
+
+// The whole of a decode call after the workspace is known.  `workspace` is
+// the caller's buffer, or (scratch_ws) the library's own device array, in
+// which case validation mode is not applied (it would allocate host memory
+// and synchronise).
+pa_status decode_call(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                      const pa_cache_desc* cache, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t max_context_len, float scale, void* out,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      void* hip_stream, bool scratch_ws) {
+    {
+        pa_status st = check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len,
+                                               num_splits, fn);
+        if (st != PA_OK) return st;
+        if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
+        if (num_seqs == 0) return ok();
+        if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+            return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
+        if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+            return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
+        const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
+                                                       max_context_len);
+        int32_t splits = resolve_splits(cache, num_q_heads, num_splits);
+        if (num_splits == 0) {
+            // No more splits than chunks can exist: small batches launch a small grid.
+            const int64_t chunk_bound = static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
+                                        group_split(cache, num_q_heads).kv_split *
+                                        ((max_tokens64 + 15) / 16);
+            splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, chunk_bound)));
+        }
+        const size_t need = workspace_for(cache, num_seqs, num_q_heads, splits);
+        if (scratch_ws) {
+            // The library's own array: checked for size before the device
+            // address is looked up (every argument check precedes it).
+            if (need > kScratchBytes)
+                return fail(PA_ERR_WORKSPACE,
+                            "%s: this call needs %zu bytes of partial results; the built-in scratch "
+                            "holds %zu (call pa_decode with a workspace instead)", fn, need, kScratchBytes);
+            const pa_status sst = scratch_for_current_device(&workspace, fn);
+            if (sst != PA_OK) return sst;
+            workspace_bytes = kScratchBytes;
+        }
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+        if (workspace_bytes < need)
+            return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+            return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+        const GroupSplit gsplit = group_split(cache, num_q_heads);
+        const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads * gsplit.kv_split;
+        if (pairs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld pairs)", fn, (long long)pairs);
+        hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+        if (validate_flag() && !scratch_ws) {
+            std::vector<int32_t> lens, tables;
+            st = fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
+            if (st != PA_OK) return st;
+            st = fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
+            if (st != PA_OK) return st;
+            for (int32_t s = 0; s < num_seqs; ++s) {
+                const int32_t L = lens[s];
+                if (L < 0 || L > max_tokens64)
+                    return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [0, %lld]", fn, s, L,
+                                (long long)max_tokens64);
+                const int32_t used = (L + cache->block_size - 1) / cache->block_size;
+                for (int32_t j = 0; j < used; ++j) {
+                    const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
+                    if (b < 0 || b >= cache->num_blocks)
+                        return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
+                }
+            }
+        }
+        DecodeArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.k_cache = static_cast<const uint16_t*>(k_cache);
+        a.v_cache = static_cast<const uint16_t*>(v_cache);
+        a.block_tables = block_tables;
+        a.context_lens = context_lens;
+        a.out = static_cast<uint16_t*>(out);
+        {
+            const size_t rows = partial_rows(cache, num_seqs, num_q_heads, splits);
+            char* ws = static_cast<char*>(workspace);
+            a.part_ml = reinterpret_cast<float*>(ws);
+            a.part_o = reinterpret_cast<float*>(ws + round_up(rows * 2 * sizeof(float)));
+        }
+        a.num_blocks = cache->num_blocks;
+        a.block_size = cache->block_size;
+        a.num_kv_heads = cache->num_kv_heads;
+        a.head_dim = cache->head_dim;
+        a.num_q_heads = num_q_heads;
+        a.num_seqs = num_seqs;
+        a.max_blocks_per_seq = max_blocks_per_seq;
+        a.max_tokens = static_cast<int32_t>(max_tokens64);
+        a.num_splits = splits;
+        a.scale_log2 = scale * kLog2e;
+        a.head_major = cache->layout == PA_LAYOUT_HEAD_MAJOR;
+        a.kv_split = gsplit.kv_split;
+        a.whole_pairs = 0;
+        if (num_splits == kWholePairs && num_seqs > 64)
+            return fail(PA_ERR_RANGE, "%s: num_splits -1 (whole pairs) takes at most 64 sequences", fn);
+        if (num_splits == kWholePairs ||
+            (num_splits == 0 && num_seqs <= 64 && max_tokens64 <= kWholePairMaxTokens)) {
+            a.whole_pairs = 1;
+            a.num_splits = static_cast<int32_t>(pairs);
+        }
+        hipError_t err = launch_decode(a, stream);
+        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+        return ok();
+    }
 }
 
 }  // namespace
@@ -254,91 +404,22 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     int32_t num_splits, void* workspace, size_t workspace_bytes,
                     void* hip_stream) {
     return pa::guard("pa_decode", [&]() -> pa_status {
-        static const char* fn = "pa_decode";
-        pa_status st = pa::check_decode_shapes(cache, num_seqs, num_q_heads, max_context_len,
-                                               num_splits, fn);
-        if (st != PA_OK) return st;
-        if (max_blocks_per_seq <= 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq must be positive", fn);
-        if (num_seqs == 0) return ok();
-        if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
-            return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
-        if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
-            return fail(PA_ERR_ALIGN, "%s: fp16 pointers must be 16-byte aligned", fn);
-        const int64_t max_tokens64 = std::min<int64_t>(static_cast<int64_t>(max_blocks_per_seq) * cache->block_size,
-                                                       max_context_len);
-        int32_t splits = pa::resolve_splits(cache, num_q_heads, num_splits);
-        if (num_splits == 0) {
-            // No more splits than chunks can exist: small batches launch a small grid.
-            const int64_t chunk_bound = static_cast<int64_t>(num_seqs) * cache->num_kv_heads *
-                                        pa::group_split(cache, num_q_heads).kv_split *
-                                        ((max_tokens64 + 15) / 16);
-            splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, chunk_bound)));
-        }
-        const size_t need = pa::workspace_for(cache, num_seqs, num_q_heads, splits);
-        if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
-        if (workspace_bytes < need)
-            return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
-        if (reinterpret_cast<uintptr_t>(workspace) % pa::kAlign != 0)
-            return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-        const pa::GroupSplit gsplit = pa::group_split(cache, num_q_heads);
-        const int64_t pairs = static_cast<int64_t>(num_seqs) * cache->num_kv_heads * gsplit.kv_split;
-        if (pairs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: launch too large (%lld pairs)", fn, (long long)pairs);
-        hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-        if (pa::validate_flag()) {
-            std::vector<int32_t> lens, tables;
-            st = pa::fetch(context_lens, static_cast<size_t>(num_seqs), lens, stream, fn);
-            if (st != PA_OK) return st;
-            st = pa::fetch(block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, tables, stream, fn);
-            if (st != PA_OK) return st;
-            for (int32_t s = 0; s < num_seqs; ++s) {
-                const int32_t L = lens[s];
-                if (L < 0 || L > max_tokens64)
-                    return fail(PA_ERR_RANGE, "%s: context_lens[%d] = %d outside [0, %lld]", fn, s, L,
-                                (long long)max_tokens64);
-                const int32_t used = (L + cache->block_size - 1) / cache->block_size;
-                for (int32_t j = 0; j < used; ++j) {
-                    const int32_t b = tables[static_cast<size_t>(s) * max_blocks_per_seq + j];
-                    if (b < 0 || b >= cache->num_blocks)
-                        return fail(PA_ERR_RANGE, "%s: block_tables[%d][%d] = %d out of range", fn, s, j, b);
-                }
-            }
-        }
-        pa::DecodeArgs a{};
-        a.q = static_cast<const uint16_t*>(q);
-        a.k_cache = static_cast<const uint16_t*>(k_cache);
-        a.v_cache = static_cast<const uint16_t*>(v_cache);
-        a.block_tables = block_tables;
-        a.context_lens = context_lens;
-        a.out = static_cast<uint16_t*>(out);
-        {
-            const size_t rows = pa::partial_rows(cache, num_seqs, num_q_heads, splits);
-            char* ws = static_cast<char*>(workspace);
-            a.part_ml = reinterpret_cast<float*>(ws);
-            a.part_o = reinterpret_cast<float*>(ws + pa::round_up(rows * 2 * sizeof(float)));
-        }
-        a.num_blocks = cache->num_blocks;
-        a.block_size = cache->block_size;
-        a.num_kv_heads = cache->num_kv_heads;
-        a.head_dim = cache->head_dim;
-        a.num_q_heads = num_q_heads;
-        a.num_seqs = num_seqs;
-        a.max_blocks_per_seq = max_blocks_per_seq;
-        a.max_tokens = static_cast<int32_t>(max_tokens64);
-        a.num_splits = splits;
-        a.scale_log2 = scale * pa::kLog2e;
-        a.head_major = cache->layout == PA_LAYOUT_HEAD_MAJOR;
-        a.kv_split = gsplit.kv_split;
-        a.whole_pairs = 0;
-        if (num_splits == pa::kWholePairs && num_seqs > 64)
-            return fail(PA_ERR_RANGE, "%s: num_splits -1 (whole pairs) takes at most 64 sequences", fn);
-        if (num_splits == pa::kWholePairs ||
-            (num_splits == 0 && num_seqs <= 64 && max_tokens64 <= pa::kWholePairMaxTokens)) {
-            a.whole_pairs = 1;
-            a.num_splits = static_cast<int32_t>(pairs);
-        }
-        hipError_t err = pa::launch_decode(a, stream);
-        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
-        return ok();
+        return pa::decode_call("pa_decode", q, k_cache, v_cache, cache, block_tables,
+                               max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                               max_context_len, scale, out, num_splits, workspace, workspace_bytes,
+                               hip_stream, false);
+    });
+}
+
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const pa_cache_desc* cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, void* out, int32_t num_splits, void* hip_stream) {
+    return pa::guard("pa_decode_noalloc", [&]() -> pa_status {
+        return pa::decode_call("pa_decode_noalloc", q, k_cache, v_cache, cache, block_tables,
+                               max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                               max_context_len, scale, out, num_splits, nullptr, 0, hip_stream, true);
     });
 }
 

@@ -62,7 +62,7 @@ NAMES = {v: k for k, v in pa.STATUS.items()}
     (dict(M=0), None, "SHAPE"),
     (dict(), _desc(d=96), "UNSUPPORTED"),
     (dict(), _desc(bs=4), "UNSUPPORTED"),
-    (dict(hq=12), None, "UNSUPPORTED"),            # group 3
+    (dict(hq=12, split=16), None, "WORKSPACE"),    # group 3 is supported: it gets to the workspace check
     (dict(split=-2), None, "RANGE"),
     (dict(split=-1, B=65, ws=0x7000, ws_bytes=1 << 30), None, "RANGE"),   # whole pairs: <= 64 seqs
     (dict(split=(1 << 20) + 1), None, "RANGE"),
@@ -215,3 +215,29 @@ def test_cache_desc_reads_the_shape_in_the_named_layout():
     assert (d.num_blocks, d.block_size, d.num_kv_heads, d.head_dim, d.layout) == (64, 4, 16, 128, 0)
     with pytest.raises(ValueError):
         pa.cache_desc(T, "column")
+
+
+def call_noalloc(desc=None, **kw):
+    args = dict(q=0x1000, k=0x2000, v=0x3000, tables=0x4000, M=4, lens=0x5000, B=4, hq=4,
+                max_ctx=33, scale=0.125, out=0x6000, split=0)
+    args.update(kw)
+    d = desc if desc is not None else _desc()
+    return pa.lib().pa_decode_noalloc(args["q"], args["k"], args["v"], ctypes.byref(d) if d else None,
+                                      args["tables"], args["M"], args["lens"], args["B"], args["hq"],
+                                      args["max_ctx"], args["scale"], args["out"], args["split"], None)
+
+
+@pytest.mark.parametrize("kw,desc,code", [
+    (dict(q=None), None, "NULL"),
+    (dict(q=0x1008), None, "ALIGN"),
+    (dict(hq=6), None, "SHAPE"),
+    (dict(), _desc(d=96), "UNSUPPORTED"),
+    (dict(split=-2), None, "RANGE"),
+    # 60000 splits of a 32-head group need more than the 8 MiB scratch
+    (dict(hq=128, split=60000, max_ctx=1 << 20, M=1 << 16), None, "WORKSPACE"),
+])
+def test_noalloc_rejects_bad_arguments_before_any_device_call(kw, desc, code):
+    """Every check (the scratch size included) runs before the scratch's
+    device address is looked up, so it also works with no GPU present."""
+    assert call_noalloc(desc, **kw) == NAMES[code]
+    assert pa.lib().pa_last_error().decode()
