@@ -118,6 +118,83 @@ struct pa_allocator {
     }
 };
 
+
+#ifdef PA_ALLOC_CHECK_INVARIANTS
+#include <cstdio>
+#include <cstdlib>
+
+namespace {
+
+[[noreturn]] void invariant_broken(const char* what, long long a, long long b) {
+    std::fprintf(stderr, "pa_allocator invariant broken: %s (%lld, %lld)\n", what, a, b);
+    std::abort();
+}
+
+// Debug builds check the whole state after every mutating call, failed calls
+// included (those must leave it unchanged, so it must still be consistent):
+//  * each block's reference count equals the number of table entries naming it;
+//  * the free list holds no block twice, only blocks with count 0, and every
+//    block with count 0 (free and used partition the pool);
+//  * a sequence holds ceil(tokens / block_size) blocks, at most the cap, all
+//    in range;
+//  * a cached prefix block is in use and indexed under its own key.
+void check_invariants(const pa_allocator* a) {
+    if (!a) return;
+    const int32_t nb = a->num_blocks;
+    std::vector<int64_t> refs(static_cast<size_t>(nb), 0);
+    for (const auto& kv : a->seqs) {
+        const Seq& s = kv.second;
+        const int64_t need = (static_cast<int64_t>(s.n_tokens) + a->block_size - 1) / a->block_size;
+        if (static_cast<int64_t>(s.blocks.size()) != need)
+            invariant_broken("sequence blocks != ceil(tokens / block_size)", s.blocks.size(), need);
+        if (static_cast<int64_t>(s.blocks.size()) > a->max_blocks_per_seq)
+            invariant_broken("sequence longer than max_blocks_per_seq", s.blocks.size(), a->max_blocks_per_seq);
+        for (int32_t b : s.blocks) {
+            if (b < 0 || b >= nb) invariant_broken("table entry out of range", b, nb);
+            ++refs[static_cast<size_t>(b)];
+        }
+    }
+    int64_t used = 0;
+    for (int32_t b = 0; b < nb; ++b) {
+        if (refs[static_cast<size_t>(b)] != a->refcount[static_cast<size_t>(b)])
+            invariant_broken("reference count != table references", refs[static_cast<size_t>(b)],
+                             a->refcount[static_cast<size_t>(b)]);
+        if (a->refcount[static_cast<size_t>(b)] > 0) ++used;
+    }
+    std::vector<char> on_list(static_cast<size_t>(nb), 0);
+    for (int32_t i = 0; i < a->free_list.size(); ++i) {
+        const int32_t b = a->free_list.at(i);
+        if (b < 0 || b >= nb) invariant_broken("free-list entry out of range", b, nb);
+        if (on_list[static_cast<size_t>(b)]) invariant_broken("block twice on the free list", b, i);
+        on_list[static_cast<size_t>(b)] = 1;
+        if (a->refcount[static_cast<size_t>(b)] != 0)
+            invariant_broken("free block with references", b, a->refcount[static_cast<size_t>(b)]);
+    }
+    if (used + a->free_list.size() != nb)
+        invariant_broken("free and used blocks do not partition the pool", used + a->free_list.size(), nb);
+    for (const auto& kv : a->cached) {
+        if (kv.first < 0 || kv.first >= nb || a->refcount[static_cast<size_t>(kv.first)] <= 0)
+            invariant_broken("cached prefix block not in use", kv.first, 0);
+        const auto it = a->prefix_index.find(kv.second.hash);
+        if (it == a->prefix_index.end() || it->second != kv.first)
+            invariant_broken("cached block not indexed under its key", kv.first, 0);
+    }
+    for (const auto& kv : a->prefix_index)
+        if (a->cached.find(kv.second) == a->cached.end())
+            invariant_broken("prefix index names an uncached block", kv.second, 0);
+}
+
+}  // namespace
+#define PA_ALLOC_CHECKED(a, call)              \
+    do {                                       \
+        const pa_status pa_st_ = (call);       \
+        check_invariants(a);                   \
+        return pa_st_;                         \
+    } while (0)
+#else
+#define PA_ALLOC_CHECKED(a, call) return (call)
+#endif
+
 using pa::fail;
 using pa::ok;
 
@@ -126,7 +203,7 @@ extern "C" {
 pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
                           int32_t max_blocks_per_seq,
                           const int32_t* initial_free_order, pa_allocator** out) {
-    return pa::guard("pa_alloc_create", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(out ? *out : nullptr, pa::guard("pa_alloc_create", [&]() -> pa_status {
         if (!out) return fail(PA_ERR_NULL, "pa_alloc_create: out is NULL");
         *out = nullptr;
         if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
@@ -151,13 +228,13 @@ pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
         }
         *out = a;
         return ok();
-    });
+    }));
 }
 
 void pa_alloc_destroy(pa_allocator* a) { delete a; }
 
 pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq, int32_t n_tokens, int32_t* slots_out) {
-    return pa::guard("pa_alloc_add_seq", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(a, pa::guard("pa_alloc_add_seq", [&]() -> pa_status {
         if (!a) return fail(PA_ERR_NULL, "pa_alloc_add_seq: allocator is NULL");
         if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq: sequence %lld exists", (long long)seq);
         if (n_tokens < 0) return fail(PA_ERR_RANGE, "pa_alloc_add_seq: negative token count");
@@ -178,11 +255,11 @@ pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq, int32_t n_tokens, int32
             for (int32_t p = 0; p < n_tokens; ++p) slots_out[p] = a->slot_of(s, p);
         a->seqs.emplace(seq, std::move(s));
         return ok();
-    });
+    }));
 }
 
 pa_status pa_alloc_fork(pa_allocator* a, int64_t parent, int64_t child) {
-    return pa::guard("pa_alloc_fork", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(a, pa::guard("pa_alloc_fork", [&]() -> pa_status {
         if (!a) return fail(PA_ERR_NULL, "pa_alloc_fork: allocator is NULL");
         auto it = a->seqs.find(parent);
         if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_fork: unknown parent %lld", (long long)parent);
@@ -192,7 +269,7 @@ pa_status pa_alloc_fork(pa_allocator* a, int64_t parent, int64_t child) {
         const auto ins = a->seqs.emplace(child, std::move(copy));
         for (int32_t b : ins.first->second.blocks) ++a->refcount[b];
         return ok();
-    });
+    }));
 }
 
 static pa_status append_one(pa_allocator* a, int64_t seq, int32_t* slot, int32_t* src, int32_t* dst) {
@@ -229,16 +306,16 @@ static pa_status append_one(pa_allocator* a, int64_t seq, int32_t* slot, int32_t
 }
 
 pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq, int32_t* slot, int32_t* cow_src, int32_t* cow_dst) {
-    return pa::guard("pa_alloc_append_slot", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(a, pa::guard("pa_alloc_append_slot", [&]() -> pa_status {
         if (!a || !slot || !cow_src || !cow_dst) return fail(PA_ERR_NULL, "pa_alloc_append_slot: NULL argument");
         pa_status st = append_one(a, seq, slot, cow_src, cow_dst);
         return st == PA_OK ? ok() : st;
-    });
+    }));
 }
 
 pa_status pa_alloc_append_batch(pa_allocator* a, const int64_t* seqs, int32_t n, int32_t* slots_out,
                                 int32_t* cow_pairs_out, int32_t* num_cow, int32_t* num_done) {
-    return pa::guard("pa_alloc_append_batch", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(a, pa::guard("pa_alloc_append_batch", [&]() -> pa_status {
         if (!a || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !num_cow || !num_done)
             return fail(PA_ERR_NULL, "pa_alloc_append_batch: NULL argument");
         if (n < 0) return fail(PA_ERR_SHAPE, "pa_alloc_append_batch: negative count");
@@ -256,11 +333,11 @@ pa_status pa_alloc_append_batch(pa_allocator* a, const int64_t* seqs, int32_t n,
             *num_done = i + 1;
         }
         return ok();
-    });
+    }));
 }
 
 pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq) {
-    return pa::guard("pa_alloc_free_seq", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(a, pa::guard("pa_alloc_free_seq", [&]() -> pa_status {
         if (!a) return fail(PA_ERR_NULL, "pa_alloc_free_seq: allocator is NULL");
         auto it = a->seqs.find(seq);
         if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_alloc_free_seq: unknown sequence %lld", (long long)seq);
@@ -276,12 +353,12 @@ pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq) {
             }
         a->seqs.erase(it);
         return ok();
-    });
+    }));
 }
 
 pa_status pa_alloc_add_seq_tokens(pa_allocator* a, int64_t seq, const int32_t* tokens,
                                   int32_t n_tokens, int32_t* slots_out, int32_t* n_cached) {
-    return pa::guard("pa_alloc_add_seq_tokens", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(a, pa::guard("pa_alloc_add_seq_tokens", [&]() -> pa_status {
         if (!a || !n_cached || (n_tokens > 0 && !tokens))
             return fail(PA_ERR_NULL, "pa_alloc_add_seq_tokens: NULL argument");
         if (a->seqs.count(seq)) return fail(PA_ERR_SEQ_EXISTS, "pa_alloc_add_seq_tokens: sequence %lld exists", (long long)seq);
@@ -335,11 +412,11 @@ pa_status pa_alloc_add_seq_tokens(pa_allocator* a, int64_t seq, const int32_t* t
         a->prefix_hits += static_cast<int64_t>(n_hit) * bs;
         *n_cached = n_hit * bs;
         return ok();
-    });
+    }));
 }
 
 pa_status pa_alloc_compact(pa_allocator* a, int32_t* pairs_out, int32_t max_pairs, int32_t* n_pairs) {
-    return pa::guard("pa_alloc_compact", [&]() -> pa_status {
+    PA_ALLOC_CHECKED(a, pa::guard("pa_alloc_compact", [&]() -> pa_status {
         if (!a || !n_pairs) return fail(PA_ERR_NULL, "pa_alloc_compact: NULL argument");
         const int32_t nb = a->num_blocks;
         int32_t used = 0;
@@ -384,7 +461,7 @@ pa_status pa_alloc_compact(pa_allocator* a, int32_t* pairs_out, int32_t max_pair
         a->free_list = FreeList(nb);       // rebuilt in increasing order even with no moves
         for (int32_t b = used; b < nb; ++b) a->free_list.push_back(b);
         return ok();
-    });
+    }));
 }
 
 pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* queried_tokens, int64_t* hit_tokens,
