@@ -676,11 +676,13 @@ __device__ __forceinline__ float tok_sum(float x) {
     return a + b;
 }
 
+// Register budget: 4 waves a SIMD (128 VGPRs) for G = 4, 3 for G = 3 (whose
+// 128-register form spills), 2 for G = 5..8.
+template <int G>
+constexpr int mfma_waves_per_simd() { return G == 4 ? 4 : (G == 3 ? 3 : 2); }
+
 template <int D, int BS, int G>
-#ifndef PA_MFMA_WAVES
-#define PA_MFMA_WAVES 4
-#endif
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? PA_MFMA_WAVES : 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<G>())))
 void decode_mfma_kernel(const DecodeArgs a) {
     static_assert(BS >= kChunk, "one block per chunk");
     constexpr int RS = mfma_row_sets<G>();        // sets of 4 query rows
