@@ -41,6 +41,8 @@
 // are masked.
 // The output is normalised once and rounded to fp16 (round to nearest even).
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace pa {
@@ -54,6 +56,8 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ constexpr h2 kOnes2 = {1.0f16, 1.0f16};
 
 constexpr float kNegBig = -1e30f;
+// Word 3 of a gfx9-family buffer resource: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kSlack = 8.0f;        // log2 units: probabilities stay below 2^8
 
 // Key position inside a 32-key group -> its column in the transposed V tile.
@@ -419,6 +423,342 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// Variant for blocks of 16 tokens or more: K and V travel from HBM straight
+// into LDS with gfx950's buffer_load ... lds (no register staging, no LDS
+// store instructions), and V stays in its natural row order.
+//  * A wave's load instruction fills 1 KiB of LDS, lane-contiguous; which
+//    global bytes each lane fetches decides the layout:
+//      K: instruction (row group rg, piece group pg) holds rows 16 rg .. +15,
+//         16-byte pieces 4 pg .. +3, lane L taking row L % 16, piece
+//         4 pg + L / 16.  A K operand read (16 rows of one piece) is then 256
+//         contiguous bytes, and successive k-steps are 512 bytes apart.
+//      V: instruction i holds whole rows (4 at D = 128, 8 at D = 64) in
+//         order; slot c of row r holds piece c ^ swz_v(r), which keeps the
+//         transposing reads below free of bank conflicts.
+//    Each instruction's rows lie in one cache block, so its buffer resource
+//    starts at that block's first such row and covers only the rows that hold
+//    tokens; rows past the context or behind an out-of-range table entry
+//    arrive as zeros.
+//  * The V^T operand of O^T += V^T P^T comes from ds_read_b64_tr_b16, whose
+//    16-lane transpose turns 4 rows x 4 columns into each lane's 4 keys of one
+//    column, in the key order the P operand needs (key bits 2 and 3 swapped,
+//    as in the register-staged kernel's slot order).
+//  * Tile t sits in stage t % 3, each stage its own LDS array so that the
+//    compiler's wait before reading a stage covers only that stage's loads
+//    (the tile loop is unrolled by three).  Iteration t fetches the block ids
+//    of tile t+3, puts tile t+2 in flight (its stage was last read in
+//    iteration t-1), computes tile t and ends at the workgroup barrier after
+//    each wave's own loads of tile t+1 have landed.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// A buffer resource over `range` bytes at `p`, built from wave-uniform values
+// (read from the first lane) so that it lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, uint32_t range) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    void* pu = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(pu, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(range)), kRsrcWord3);
+}
+
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4v lds_s4v;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int S>
+struct Stage {};
+
+template <int D, int KT, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a) {
+    constexpr int kRowB = D * 2;                      // bytes of a row
+    constexpr int kP = D / 8;                         // 16-byte pieces of a row
+    constexpr int kPG = kP / 4;                       // K piece groups of a row
+    constexpr int kVRows = 64 / kP;                   // rows of one V instruction
+    constexpr int kInstTile = KT * kP / 64;           // instructions per matrix and tile
+    constexpr int kInst = kInstTile / kWaves;         // of them, per wave
+    static_assert(kInst >= 1 && kInst * kWaves == kInstTile && KT % 16 == 0, "whole instructions per wave");
+    constexpr int kSub = KT / 32;                     // 32-key sub-tiles per tile
+    constexpr int kDT = D / 32;                       // 32-wide output column tiles
+    constexpr int kQS = D / 16;                       // k-steps of the QK contraction
+    constexpr int kTileB = KT * kRowB;                // one matrix of one tile
+    __shared__ __align__(16) unsigned char st0[2 * kTileB];
+    __shared__ __align__(16) unsigned char st1[2 * kTileB];
+    __shared__ __align__(16) unsigned char st2[2 * kTileB];
+
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int items = a.num_seqs * a.num_kv_heads * a.tiles_per_seq;
+    const int item = work_item(blockIdx.x, gridDim.x);
+    if (item >= items) return;
+    const int tile = item % a.tiles_per_seq;
+    const int sg = item / a.tiles_per_seq;
+    const int g = sg % a.num_kv_heads;
+    const int s = sg / a.num_kv_heads;
+
+    const int qs = a.query_start[s];
+    if (qs < 0 || qs > a.num_tokens) return;
+    int L = a.context_lens[s];
+    L = L < 0 ? 0 : (L > a.max_tokens ? a.max_tokens : L);
+    int n = a.query_start[s + 1] - qs;
+    n = n < 0 ? 0 : (n > L ? L : n);
+    n = n > a.num_tokens - qs ? a.num_tokens - qs : n;
+    const int rows = n * G;
+    const int row0 = tile * 32 * kWaves;
+    if (row0 >= rows) return;
+    L = __builtin_amdgcn_readfirstlane(L);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m = lane & 31;
+    const int hi = lane >> 5;
+    const int first = L - n;                          // position of chunk row 0
+
+    const int w_row_lo = row0 + wave * 32;
+    const bool wave_on = w_row_lo < rows;
+    const int w_row_hi = min(w_row_lo + 31, rows - 1);
+    const int w_pos_lo = first + w_row_lo / G;
+    const int w_pos_hi = first + w_row_hi / G;
+    const int n_keys = first + (min(row0 + 32 * kWaves, rows) - 1) / G + 1;
+    const int n_tiles = (n_keys + KT - 1) / KT;
+
+    // This lane's query row and its Q^T operands.
+    const int r_q = w_row_lo + m;
+    const bool row_ok = r_q < rows;
+    const int re = row_ok ? r_q : rows - 1;
+    const int jj = re / G;
+    const int row_tok = qs + jj;
+    const int row_head = g * G + (re - jj * G);
+    const int row_pos = first + jj;
+    h8 qv[kQS];
+    {
+        const _Float16* qp = reinterpret_cast<const _Float16*>(a.q) +
+                             (static_cast<size_t>(row_tok) * a.num_q_heads + row_head) * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < kQS; ++ks) qv[ks] = *reinterpret_cast<const h8*>(qp + 16 * ks);
+    }
+    // Let the Q rows land before the loads of the tile loop are counted (so
+    // that no wait inside the loop is for them).
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+
+    const int bshift = a.block_shift;
+    const int bmask = (1 << bshift) - 1;
+    const int* table = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
+    const uint32_t tok_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+    const size_t block_bytes = static_cast<size_t>(a.block_size) * a.num_kv_heads * D * 2;
+    const size_t head_off = static_cast<size_t>(g) * D * 2 * (a.head_major ? a.block_size : 1);
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k_cache) + head_off;
+    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v_cache) + head_off;
+    // Per-lane global offsets of the load instructions (relative to their
+    // first row): K row L % 16, piece 4 pg + L / 16; V row L / P, the piece
+    // that its slot L % P holds.
+    const uint32_t k_lane = static_cast<uint32_t>(lane & 15) * tok_bytes + 16u * (lane >> 4);
+    const int v_row = lane / kP;
+    const uint32_t v_lane = static_cast<uint32_t>(v_row) * tok_bytes + 16u * ((lane % kP) ^ swz_v<D>(v_row));
+
+    // Block ids of tile k0: lane u < kInst holds that of this wave's
+    // instruction u (K row group and V rows share one 16-token group); keys
+    // past the context read entry 0, which every table has.
+    auto fetch_ids = [&](int k0) __attribute__((always_inline)) -> int {
+        const int inst = wave * kInst + (lane < kInst ? lane : 0);
+        const int key = k0 + 16 * (inst / kPG);
+        return table[key < L ? key >> bshift : 0];
+    };
+    auto issue_tile = [&](int k0, int ids, unsigned char* stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kInst; ++u) {
+            const int inst = wave * kInst + u;
+            int b = __builtin_amdgcn_readlane(ids, u);
+            const bool b_ok = b >= 0 && b < a.num_blocks;
+            b = b_ok ? b : 0;
+            const size_t blk = static_cast<size_t>(b) * block_bytes;
+            // K: rows 16 * (inst / kPG) .., pieces 4 * (inst % kPG) ..
+            const int kkey = k0 + 16 * (inst / kPG);
+            int kval = L - kkey;
+            kval = !b_ok || kval < 0 ? 0 : (kval > 16 ? 16 : kval);
+            const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(
+                kbase + blk + static_cast<size_t>(kkey & bmask) * tok_bytes, static_cast<uint32_t>(kval) * tok_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + inst * 1024), 16,
+                                                     k_lane + 64u * (inst % kPG), 0, 0, 0);
+            // V: rows kVRows * inst ..
+            const int vkey = k0 + kVRows * inst;
+            int vval = L - vkey;
+            vval = !b_ok || vval < 0 ? 0 : (vval > kVRows ? kVRows : vval);
+            const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(
+                vbase + blk + static_cast<size_t>(vkey & bmask) * tok_bytes, static_cast<uint32_t>(vval) * tok_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + kTileB + inst * 1024), 16, v_lane, 0, 0, 0);
+        }
+    };
+
+    // Fixed per-lane parts of the LDS operand reads.
+    //  K (A operand of S^T): row 32 st + m, piece 2 ks + hi.
+    const uint32_t k_rd = static_cast<uint32_t>((m >> 4) * kPG * 1024 + hi * 256 + (m & 15) * 16);
+    //  V (transposing read, as a source lane 16 gg + 4 e + q): row
+    //  16 ks + 8 h + 4 (gg / 2) + e, columns 32 dt + 16 (gg % 2) + 4 q .. + 3.
+    const int gg = lane >> 4, ve = (lane >> 2) & 3, vq = lane & 3;
+    const int v_r = 4 * (gg >> 1) + ve;               // row, less 16 ks + 8 h
+    uint32_t v_rd[kDT];
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+        const int piece = 4 * dt + 2 * (gg & 1) + (vq >> 1);
+        v_rd[dt] = static_cast<uint32_t>(kTileB + v_r * kRowB + 16 * (piece ^ swz_v<D>(v_r)) + 8 * (vq & 1));
+    }
+
+    f16x acc_o[kDT];
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.0f;
+    float m_ref = kNegBig;                            // reference max (log2 units)
+    float l_sum = 0.0f;                               // this half-wave's keys only
+    const float c_log2 = a.scale_log2;
+
+    auto compute = [&](const unsigned char* kt, int k0) __attribute__((always_inline)) {
+        f16x sacc[kSub];
+        h8 kop[kSub][kQS];
+#pragma unroll
+        for (int st = 0; st < kSub; ++st)
+#pragma unroll
+            for (int ks = 0; ks < kQS; ++ks)
+                kop[st][ks] = *reinterpret_cast<const h8*>(kt + k_rd + st * 2 * kPG * 1024 + ks * 512);
+#pragma unroll
+        for (int st = 0; st < kSub; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[st][r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kQS; ++ks)
+#pragma unroll
+            for (int st = 0; st < kSub; ++st)
+                sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[st][ks], qv[ks], sacc[st], 0, 0, 0);
+        h8 vop[kDT][2 * kSub];
+#pragma unroll
+        for (int ks = 0; ks < 2 * kSub; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt) {
+                const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s4v*)(kt + v_rd[dt] + (16 * ks) * kRowB));
+                const s4v up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s4v*)(kt + v_rd[dt] + (16 * ks + 8) * kRowB));
+                vop[dt][ks] = __builtin_bit_cast(h8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        if (k0 + KT - 1 > w_pos_lo) {
+#pragma unroll
+            for (int st = 0; st < kSub; ++st)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * st + (r >> 2) * 8 + 4 * hi + (r & 3);
+                    if (key > row_pos) sacc[st][r] = kNegBig;
+                }
+        }
+        float mv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mv[i] = kNegBig;
+#pragma unroll
+        for (int st = 0; st < kSub; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mv[r & 7] = fmaxf(mv[r & 7], sacc[st][r]);
+        float mx = fmaxf(fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])),
+                         fmaxf(fmaxf(mv[4], mv[5]), fmaxf(mv[6], mv[7])));
+        {
+            float ma, mb;
+            halves(mx, ma, mb);
+            mx = fmaxf(ma, mb) * c_log2;
+        }
+        const bool grow = mx > m_ref + kSlack;
+        if (__ballot(grow)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_sum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+        }
+        h8 pb[2 * kSub];
+#pragma unroll
+        for (int st = 0; st < kSub; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][r], c_log2, -m_ref));
+                pb[2 * st + (r >> 3)][r & 7] = static_cast<_Float16>(p);
+            }
+#pragma unroll
+        for (int ks = 0; ks < 2 * kSub; ++ks)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const h2 pp = {pb[ks][2 * e2], pb[ks][2 * e2 + 1]};
+                l_sum = __builtin_amdgcn_fdot2(pp, kOnes2, l_sum, false);
+            }
+#pragma unroll
+        for (int ks = 0; ks < 2 * kSub; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < kDT; ++dt)
+                acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[dt][ks], pb[ks], acc_o[dt], 0, 0, 0);
+    };
+
+    // Wait until this wave's loads of the next tile have landed (at most the
+    // block-id fetch and the loads issued after them are outstanding), then
+    // meet the workgroup.
+    auto wait_and_barrier = [&]() __attribute__((always_inline)) {
+        if constexpr (kInst == 2)
+            asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+    };
+    auto stage_of = [&](auto sc) __attribute__((always_inline)) -> unsigned char* {
+        if constexpr (std::is_same<decltype(sc), Stage<0>>::value) return st0;
+        else if constexpr (std::is_same<decltype(sc), Stage<1>>::value) return st1;
+        else return st2;
+    };
+
+    // Prologue: tiles 0 and 1 in flight, the ids of tile 2 fetched between
+    // them (every iteration fetches ids before it issues loads, so waiting for
+    // a tile's ids never waits for loads issued after them).
+    const int ids0 = fetch_ids(0);
+    const int ids1 = fetch_ids(KT);
+    issue_tile(0, ids0, st0);
+    int ids_next = fetch_ids(2 * KT);                 // ids of tile t + 2
+    issue_tile(KT, ids1, st1);
+    wait_and_barrier();
+
+    auto step = [&](auto cur, auto ahead, int t) __attribute__((always_inline)) {
+        const int k0 = t * KT;
+        const int ids3 = fetch_ids(k0 + 3 * KT);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_tile(k0 + 2 * KT, ids_next, stage_of(ahead));
+        __builtin_amdgcn_sched_barrier(0);
+        ids_next = ids3;
+        if (wave_on && k0 <= w_pos_hi) compute(stage_of(cur), k0);
+        wait_and_barrier();
+    };
+    for (int t = 0; t < n_tiles; t += 3) {
+        step(Stage<0>{}, Stage<2>{}, t);
+        if (t + 1 >= n_tiles) break;
+        step(Stage<1>{}, Stage<0>{}, t + 1);
+        if (t + 2 >= n_tiles) break;
+        step(Stage<2>{}, Stage<1>{}, t + 2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    float la, lb;
+    halves(l_sum, la, lb);
+    const float l_tot = la + lb;
+    if (!row_ok) return;
+    const float inv = 1.0f / l_tot;
+    _Float16* op = reinterpret_cast<_Float16*>(a.out) +
+                   (static_cast<size_t>(row_tok) * a.num_q_heads + row_head) * D + 4 * hi;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            h4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = static_cast<_Float16>(acc_o[dt][4 * rq + i] * inv);
+            *reinterpret_cast<h4*>(op + 32 * dt + 8 * rq) = o;
+        }
+}
+
 template <int D, int KT, int kWaves, int kNT>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const uint64_t cache_bytes = static_cast<uint64_t>(a.num_blocks) * a.block_size * a.num_kv_heads * D * 2;
@@ -431,7 +771,10 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     if (items == 0) return hipSuccess;
     const int64_t grid = (items + 7) / 8 * 8;
     if (grid > INT32_MAX) return hipErrorInvalidValue;
-    if (cache_bytes <= UINT32_MAX)
+    if (kNT == 1 && a.block_size >= 16)
+        hipLaunchKernelGGL((prefill_lds_kernel<D, KT, kWaves>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kWaves * 64), 0, stream, b);
+    else if (cache_bytes <= UINT32_MAX)
         hipLaunchKernelGGL((prefill_kernel<D, KT, kWaves, kNT, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(kWaves * 64), 0, stream, b);
     else
