@@ -435,20 +435,22 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 //      V: instruction i holds whole rows (4 at D = 128, 8 at D = 64) in
 //         order; slot c of row r holds piece c ^ swz_v(r), which keeps the
 //         transposing reads below free of bank conflicts.
-//    Each instruction's rows lie in one cache block, so its buffer resource
-//    starts at that block's first such row and covers only the rows that hold
-//    tokens; rows past the context or behind an out-of-range table entry
-//    arrive as zeros.
+//    A wave's instructions cover one 16-token group of a stage, which lies
+//    in one cache block: one block id and one buffer resource per matrix,
+//    starting at the group's first row and covering only the rows that hold
+//    tokens (rows past the keys this workgroup sees, or behind an
+//    out-of-range table entry, arrive as zeros); the instructions differ in
+//    the scalar offset (which the range check covers) and the LDS address.
 //  * The V^T operand of O^T += V^T P^T comes from ds_read_b64_tr_b16, whose
 //    16-lane transpose turns 4 rows x 4 columns into each lane's 4 keys of one
 //    column, in the key order the P operand needs (key bits 2 and 3 swapped,
 //    as in the register-staged kernel's slot order).
-//  * Tile t sits in stage t % 3, each stage its own LDS array so that the
-//    compiler's wait before reading a stage covers only that stage's loads
-//    (the tile loop is unrolled by three).  Iteration t fetches the block ids
-//    of tile t+3, puts tile t+2 in flight (its stage was last read in
-//    iteration t-1), computes tile t and ends at the workgroup barrier after
-//    each wave's own loads of tile t+1 have landed.
+//  * Tile t (KT = 64 keys) sits in stage t % 3; the stages are separate LDS
+//    arrays so that the compiler's own wait before reading one covers only
+//    that stage's loads (the loop is unrolled by three).  Iteration t fetches
+//    the block ids of tile t + 3, puts tile t + 2 in flight (into the stage
+//    that iteration t - 1 finished reading), computes tile t, and ends at the
+//    workgroup barrier once each wave's own loads of tile t + 1 have landed.
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
@@ -469,16 +471,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int S>
 struct Stage {};
 
-template <int D, int KT, int kWaves>
+template <int D, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a) {
+    constexpr int KT = 64;                            // keys of a tile
     constexpr int kRowB = D * 2;                      // bytes of a row
     constexpr int kP = D / 8;                         // 16-byte pieces of a row
     constexpr int kPG = kP / 4;                       // K piece groups of a row
     constexpr int kVRows = 64 / kP;                   // rows of one V instruction
     constexpr int kInstTile = KT * kP / 64;           // instructions per matrix and tile
     constexpr int kInst = kInstTile / kWaves;         // of them, per wave
-    static_assert(kInst >= 1 && kInst * kWaves == kInstTile && KT % 16 == 0, "whole instructions per wave");
-    constexpr int kSub = KT / 32;                     // 32-key sub-tiles per tile
+    static_assert(kInst * kWaves == kInstTile && kPG % kInst == 0, "a wave's K instructions in one row group");
+    static_assert(kInst * 64 / kP <= 16 && 16 % (kInst * 64 / kP) == 0, "a wave's rows in one 16-token group");
+    constexpr int kSub = KT / 32;                     // 32-key sub-tiles of a tile
     constexpr int kDT = D / 32;                       // 32-wide output column tiles
     constexpr int kQS = D / 16;                       // k-steps of the QK contraction
     constexpr int kTileB = KT * kRowB;                // one matrix of one tile
@@ -505,7 +509,6 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
     const int rows = n * G;
     const int row0 = tile * 32 * kWaves;
     if (row0 >= rows) return;
-    L = __builtin_amdgcn_readfirstlane(L);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -518,7 +521,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
     const int w_row_hi = min(w_row_lo + 31, rows - 1);
     const int w_pos_lo = first + w_row_lo / G;
     const int w_pos_hi = first + w_row_hi / G;
-    const int n_keys = first + (min(row0 + 32 * kWaves, rows) - 1) / G + 1;
+    // Keys this workgroup's rows see: the loads stop there.
+    const int n_keys = __builtin_amdgcn_readfirstlane(first + (min(row0 + 32 * kWaves, rows) - 1) / G + 1);
     const int n_tiles = (n_keys + KT - 1) / KT;
 
     // This lane's query row and its Q^T operands.
@@ -554,42 +558,40 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
     const uint32_t k_lane = static_cast<uint32_t>(lane & 15) * tok_bytes + 16u * (lane >> 4);
     const int v_row = lane / kP;
     const uint32_t v_lane = static_cast<uint32_t>(v_row) * tok_bytes + 16u * ((lane % kP) ^ swz_v<D>(v_row));
+    const int inst0 = wave * kInst;                   // this wave's first instruction of a stage
 
-    // Block ids of tile k0: lane u < kInst holds that of this wave's
-    // instruction u (K row group and V rows share one 16-token group); keys
-    // past the context read entry 0, which every table has.
+    // Block id of this wave's 16-token group of tile k0 (keys past the
+    // workgroup's keys read entry 0, which every table has).
     auto fetch_ids = [&](int k0) __attribute__((always_inline)) -> int {
-        const int inst = wave * kInst + (lane < kInst ? lane : 0);
-        const int key = k0 + 16 * (inst / kPG);
-        return table[key < L ? key >> bshift : 0];
+        const int key = k0 + 16 * (inst0 / kPG);
+        return table[key < n_keys ? key >> bshift : 0];
     };
     auto issue_tile = [&](int k0, int ids, unsigned char* stage) __attribute__((always_inline)) {
+        int b = __builtin_amdgcn_readfirstlane(ids);
+        const bool b_ok = b >= 0 && b < a.num_blocks;
+        b = b_ok ? b : 0;
+        const size_t blk = static_cast<size_t>(b) * block_bytes;
+        const int kkey = k0 + 16 * (inst0 / kPG);
+        int kval = n_keys - kkey;
+        kval = !b_ok || kval < 0 ? 0 : (kval > 16 ? 16 : kval);
+        const int vkey = k0 + kVRows * inst0;
+        int vval = n_keys - vkey;
+        vval = !b_ok || vval < 0 ? 0 : (vval > kVRows * kInst ? kVRows * kInst : vval);
+        const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(
+            kbase + blk + static_cast<size_t>(kkey & bmask) * tok_bytes, static_cast<uint32_t>(kval) * tok_bytes);
+        const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(
+            vbase + blk + static_cast<size_t>(vkey & bmask) * tok_bytes, static_cast<uint32_t>(vval) * tok_bytes);
+        const uint32_t k_off = k_lane + 64u * (inst0 % kPG);
 #pragma unroll
         for (int u = 0; u < kInst; ++u) {
-            const int inst = wave * kInst + u;
-            int b = __builtin_amdgcn_readlane(ids, u);
-            const bool b_ok = b >= 0 && b < a.num_blocks;
-            b = b_ok ? b : 0;
-            const size_t blk = static_cast<size_t>(b) * block_bytes;
-            // K: rows 16 * (inst / kPG) .., pieces 4 * (inst % kPG) ..
-            const int kkey = k0 + 16 * (inst / kPG);
-            int kval = L - kkey;
-            kval = !b_ok || kval < 0 ? 0 : (kval > 16 ? 16 : kval);
-            const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(
-                kbase + blk + static_cast<size_t>(kkey & bmask) * tok_bytes, static_cast<uint32_t>(kval) * tok_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + inst * 1024), 16,
-                                                     k_lane + 64u * (inst % kPG), 0, 0, 0);
-            // V: rows kVRows * inst ..
-            const int vkey = k0 + kVRows * inst;
-            int vval = L - vkey;
-            vval = !b_ok || vval < 0 ? 0 : (vval > kVRows ? kVRows : vval);
-            const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(
-                vbase + blk + static_cast<size_t>(vkey & bmask) * tok_bytes, static_cast<uint32_t>(vval) * tok_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + kTileB + inst * 1024), 16, v_lane, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + (inst0 + u) * 1024), 16, k_off, 64 * u, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + kTileB + (inst0 + u) * 1024), 16, v_lane,
+                                                     u * kVRows * static_cast<int>(tok_bytes), 0, 0);
         }
     };
 
-    // Fixed per-lane parts of the LDS operand reads.
+    // Fixed per-lane parts of the LDS operand reads, relative to a tile's K
+    // and V.
     //  K (A operand of S^T): row 32 st + m, piece 2 ks + hi.
     const uint32_t k_rd = static_cast<uint32_t>((m >> 4) * kPG * 1024 + hi * 256 + (m & 15) * 16);
     //  V (transposing read, as a source lane 16 gg + 4 e + q): row
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
         const int piece = 4 * dt + 2 * (gg & 1) + (vq >> 1);
-        v_rd[dt] = static_cast<uint32_t>(kTileB + v_r * kRowB + 16 * (piece ^ swz_v<D>(v_r)) + 8 * (vq & 1));
+        v_rd[dt] = static_cast<uint32_t>(v_r * kRowB + 16 * (piece ^ swz_v<D>(v_r)) + 8 * (vq & 1));
     }
 
     f16x acc_o[kDT];
@@ -612,8 +614,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
     float l_sum = 0.0f;                               // this half-wave's keys only
     const float c_log2 = a.scale_log2;
 
-    auto compute = [&](const unsigned char* kt, int k0) __attribute__((always_inline)) {
-        f16x sacc[kSub];
+    // One 64-key half: K rows at kt (row-group layout), V rows at vt.
+    f16x sacc[kSub];
+    // S^T = K Q^T of the tile whose K rows are at kt.
+    auto qk = [&](const unsigned char* kt) __attribute__((always_inline)) {
         h8 kop[kSub][kQS];
 #pragma unroll
         for (int st = 0; st < kSub; ++st)
@@ -629,15 +633,18 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
 #pragma unroll
             for (int st = 0; st < kSub; ++st)
                 sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[st][ks], qv[ks], sacc[st], 0, 0, 0);
+    };
+    // Softmax and O^T += V^T P^T of the tile whose V rows are at vt.
+    auto rest = [&](const unsigned char* vt, int k0) __attribute__((always_inline)) {
         h8 vop[kDT][2 * kSub];
 #pragma unroll
         for (int ks = 0; ks < 2 * kSub; ++ks)
 #pragma unroll
             for (int dt = 0; dt < kDT; ++dt) {
                 const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s4v*)(kt + v_rd[dt] + (16 * ks) * kRowB));
+                    (lds_s4v*)(vt + v_rd[dt] + (16 * ks) * kRowB));
                 const s4v up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s4v*)(kt + v_rd[dt] + (16 * ks + 8) * kRowB));
+                    (lds_s4v*)(vt + v_rd[dt] + (16 * ks + 8) * kRowB));
                 vop[dt][ks] = __builtin_bit_cast(h8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         __builtin_amdgcn_sched_barrier(0);
@@ -697,14 +704,15 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
                 acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[dt][ks], pb[ks], acc_o[dt], 0, 0, 0);
     };
 
-    // Wait until this wave's loads of the next tile have landed (at most the
-    // block-id fetch and the loads issued after them are outstanding), then
-    // meet the workgroup.
+    // Each wave waits for its own loads of the next tile (at most the loads
+    // and id fetch issued after them still outstanding), then the workgroup
+    // meets.  The wait is the compiler's own instruction, so that
+    // its bookkeeping knows which loads have landed.
+    constexpr int kAfter = 2 * kInst + 1;            // id fetch + loads of the tile after
+    static_assert(kAfter < 16, "vmcnt field");
     auto wait_and_barrier = [&]() __attribute__((always_inline)) {
-        if constexpr (kInst == 2)
-            asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kAfter);
+        asm volatile("s_barrier" ::: "memory");
     };
     auto stage_of = [&](auto sc) __attribute__((always_inline)) -> unsigned char* {
         if constexpr (std::is_same<decltype(sc), Stage<0>>::value) return st0;
@@ -713,23 +721,29 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_lds_kernel(PrefillArgs a)
     };
 
     // Prologue: tiles 0 and 1 in flight, the ids of tile 2 fetched between
-    // them (every iteration fetches ids before it issues loads, so waiting for
-    // a tile's ids never waits for loads issued after them).
-    const int ids0 = fetch_ids(0);
-    const int ids1 = fetch_ids(KT);
-    issue_tile(0, ids0, st0);
-    int ids_next = fetch_ids(2 * KT);                 // ids of tile t + 2
-    issue_tile(KT, ids1, st1);
-    wait_and_barrier();
-
+    // them (every iteration fetches ids before it issues loads, so that
+    // waiting for a tile's ids never waits for loads issued after them).
+    int ids_next;                                     // ids of tile t + 2
+    {
+        const int ids0 = fetch_ids(0);
+        const int ids1 = fetch_ids(KT);
+        issue_tile(0, ids0, st0);
+        ids_next = fetch_ids(2 * KT);
+        issue_tile(KT, ids1, st1);
+        wait_and_barrier();
+    }
     auto step = [&](auto cur, auto ahead, int t) __attribute__((always_inline)) {
         const int k0 = t * KT;
-        const int ids3 = fetch_ids(k0 + 3 * KT);
+        const int ids_new = fetch_ids(k0 + 3 * KT);
         __builtin_amdgcn_sched_barrier(0);
         issue_tile(k0 + 2 * KT, ids_next, stage_of(ahead));
         __builtin_amdgcn_sched_barrier(0);
-        ids_next = ids3;
-        if (wave_on && k0 <= w_pos_hi) compute(stage_of(cur), k0);
+        ids_next = ids_new;
+        if (wave_on && k0 <= w_pos_hi) {
+            const unsigned char* sp = stage_of(cur);
+            qk(sp);
+            rest(sp + kTileB, k0);
+        }
         wait_and_barrier();
     };
     for (int t = 0; t < n_tiles; t += 3) {
@@ -772,7 +786,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const int64_t grid = (items + 7) / 8 * 8;
     if (grid > INT32_MAX) return hipErrorInvalidValue;
     if (kNT == 1 && a.block_size >= 16)
-        hipLaunchKernelGGL((prefill_lds_kernel<D, KT, kWaves>), dim3(static_cast<unsigned>(grid)),
+        hipLaunchKernelGGL((prefill_lds_kernel<D, kWaves>), dim3(static_cast<unsigned>(grid)),
                            dim3(kWaves * 64), 0, stream, b);
     else if (cache_bytes <= UINT32_MAX)
         hipLaunchKernelGGL((prefill_kernel<D, KT, kWaves, kNT, true>), dim3(static_cast<unsigned>(grid)),
