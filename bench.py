@@ -283,17 +283,17 @@ def read_ceiling(buffers, reps):
     median launch is reported."""
     import torch
 
-    import paged_kv_cache_382_amd as pa
+    from paged_kv_cache_382_amd import probe
     sink = torch.zeros(1, dtype=torch.int32, device=buffers[0].device)
     for b in buffers:
-        pa.pa_read_probe(b, sink)
+        probe.pa_read_probe(b, sink)
     torch.cuda.synchronize()
     times, nbytes = [], []
     for _ in range(reps):
         for b in buffers:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            pa.pa_read_probe(b, sink)
+            probe.pa_read_probe(b, sink)
             e1.record()
             times.append((e0, e1))
             nbytes.append(b.numel() * b.element_size())

@@ -243,24 +243,6 @@ int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads,
                              int32_t num_splits);
 
 /* ----------------------------------------------------------------------- */
-/* Streaming-read probe: a measurement helper, not a step of the attention
- * path.  [vLLM-core] section 3 ("Continuous batching") ties decode speed to
- * memory bandwidth; this call reads a buffer once at the rate the device
- * streams plain reads, so that the decode kernel's bandwidth can be set
- * beside it in the same run on the same memory.
- *
- *   buf     device, 16-byte aligned, `bytes` readable bytes; read once with
- *           16-byte non-temporal loads spread over the whole device
- *   bytes   a multiple of 16; 0 launches nothing
- *   sink    device uint32, 4-byte aligned: written (with 0x9E3779B9) only if
- *           the XOR of the 32-bit words one lane read equals 0x9E3779B9, so
- *           the loads cannot be optimised away; normally left untouched
- *
- * Enqueued on hip_stream; returns after the launch.  Errors: PA_ERR_SHAPE
- * (bytes not a multiple of 16), PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_HIP. */
-pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream);
-
-/* ----------------------------------------------------------------------- */
 /* Chunked prefill: causal attention of packed prompt chunks over the cache.
  *
  * Sources: [PA-mem] "Deployable configuration parameters" (prompts are
@@ -326,7 +308,7 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
  */
 typedef struct pa_allocator pa_allocator;
 
-typedef struct pa_alloc_stats {
+typedef struct pa_alloc_stats_t {
     int32_t num_blocks;
     int32_t free_blocks;
     int32_t used_blocks;            /* reference count > 0                    */
@@ -337,7 +319,7 @@ typedef struct pa_alloc_stats {
     int64_t stored_tokens;          /* filled slots of used blocks            */
     double utilisation;             /* used_blocks / num_blocks               */
     double internal_fragmentation;  /* empty slots / slots of used blocks     */
-} pa_alloc_stats;
+} pa_alloc_stats_t;
 
 /* Create an allocator.  block_size and max_blocks_per_seq must be positive. */
 pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
@@ -379,7 +361,8 @@ pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seqs, int32_t n,
                           int32_t row_stride, int32_t* block_tables_out,
                           int32_t* context_lens_out);
 
-pa_status pa_alloc_get_stats(const pa_allocator* a, pa_alloc_stats* out);
+/* Counters of the allocator's state (copied into *out). */
+pa_status pa_alloc_stats(const pa_allocator* a, pa_alloc_stats_t* out);
 
 /* Reference count of a block, or -1 if out of range. */
 int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);

@@ -77,7 +77,6 @@ SIGNATURES = {
     "pa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P, _I32,
                                          _I32, _I32, ctypes.c_float, _P, _I32, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32]),
-    "pa_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "pa_decode_num_splits": (_I32, [ctypes.POINTER(CacheDesc), _I32, _I32]),
     "pa_prefill": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(CacheDesc), _P, _I32, _P, _P, _I32,
                                   _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P]),
@@ -89,7 +88,7 @@ SIGNATURES = {
     "pa_alloc_append_batch": (ctypes.c_int, [_P, _PI64, _I32, _PI32, _PI32, _PI32, _PI32]),
     "pa_alloc_free_seq": (ctypes.c_int, [_P, _I64]),
     "pa_alloc_export": (ctypes.c_int, [_P, _PI64, _I32, _I32, _PI32, _PI32]),
-    "pa_alloc_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(AllocStats)]),
+    "pa_alloc_stats": (ctypes.c_int, [_P, ctypes.POINTER(AllocStats)]),
     "pa_alloc_refcount": (_I32, [_P, _I32]),
     "pa_alloc_num_free": (_I32, [_P]),
     "pa_alloc_free_list": (_I32, [_P, _PI32, _I32]),
@@ -202,17 +201,6 @@ def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None, layout="slot"):
         _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
         ctypes.byref(desc), _dev(src_dst, torch.int32, "src_dst") if n else None, n,
         _stream(stream)))
-
-
-def pa_read_probe(buf, sink, stream=None):
-    """Read every byte of the contiguous device tensor ``buf`` once (the
-    streaming-read probe; ``sink`` is a one-element int32 device tensor)."""
-    import torch
-    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
-        raise ValueError("buf must be a contiguous device tensor")
-    nbytes = buf.numel() * buf.element_size()
-    _check(lib().pa_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes,
-                               _dev(sink, torch.int32, "sink"), _stream(stream)))
 
 
 def pa_decode_workspace_bytes(desc, num_seqs, num_q_heads, num_splits=0):
@@ -496,7 +484,7 @@ class Allocator:
 
     def stats(self):
         st = AllocStats()
-        _check(lib().pa_alloc_get_stats(self._h, ctypes.byref(st)))
+        _check(lib().pa_alloc_stats(self._h, ctypes.byref(st)))
         return {name: getattr(st, name) for name, _ in AllocStats._fields_}
 
     def refcount(self, block):

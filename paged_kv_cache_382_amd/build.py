@@ -18,6 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libpa.so")
+# The streaming-read probe (a measurement helper, include/pa_probe.h) is a
+# library of its own, so that the attention library holds only the path.
+PROBE_LIB = os.path.join(LIB_DIR, "libpa_probe.so")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -37,8 +40,8 @@ SOURCES = [
     ("store_kvcache.hip", "hip"),
     ("decode.hip", "hip"),
     ("prefill.hip", "hip"),
-    ("probe.hip", "hip"),
 ]
+PROBE_SOURCES = [("probe.hip", "hip")]
 
 
 def _compile(src, kind, extra):
@@ -63,15 +66,17 @@ def build(verbose=False, extra_hip_flags=()):
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda sk: _compile(sk[0], sk[1], extra_hip_flags), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    shutil.move(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+        objs = list(ex.map(lambda sk: _compile(sk[0], sk[1], extra_hip_flags), SOURCES + PROBE_SOURCES))
+    n_main = len(SOURCES)
+    for target, parts in ((LIB, objs[:n_main]), (PROBE_LIB, objs[n_main:])):
+        tmp = target + ".tmp"
+        cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + parts
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        shutil.move(tmp, target)
+        if verbose:
+            print(f"built {target}")
     return LIB
 
 

@@ -499,9 +499,9 @@ pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seqs, int32_t n,
     });
 }
 
-pa_status pa_alloc_get_stats(const pa_allocator* a, pa_alloc_stats* out) {
-    return pa::guard("pa_alloc_get_stats", [&]() -> pa_status {
-        if (!a || !out) return fail(PA_ERR_NULL, "pa_alloc_get_stats: NULL argument");
+pa_status pa_alloc_stats(const pa_allocator* a, pa_alloc_stats_t* out) {
+    return pa::guard("pa_alloc_stats", [&]() -> pa_status {
+        if (!a || !out) return fail(PA_ERR_NULL, "pa_alloc_stats: NULL argument");
         std::vector<int32_t> fill(static_cast<size_t>(a->num_blocks), 0);
         int64_t logical = 0;
         for (const auto& kv : a->seqs) {

@@ -367,21 +367,6 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
     });
 }
 
-pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream) {
-    return pa::guard("pa_read_probe", [&]() -> pa_status {
-        static const char* fn = "pa_read_probe";
-        if (bytes % 16 != 0) return fail(PA_ERR_SHAPE, "%s: bytes (%zu) must be a multiple of 16", fn, bytes);
-        if (bytes == 0) return ok();
-        if (!buf || !sink) return fail(PA_ERR_NULL, "%s: NULL pointer", fn);
-        if (!pa::aligned16(buf)) return fail(PA_ERR_ALIGN, "%s: buffer must be 16-byte aligned", fn);
-        if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return fail(PA_ERR_ALIGN, "%s: sink must be 4-byte aligned", fn);
-        hipError_t err = pa::launch_read_probe(buf, static_cast<int64_t>(bytes / 16), sink,
-                                               static_cast<hipStream_t>(hip_stream));
-        if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
-        return ok();
-    });
-}
-
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_splits) {
     if (pa::check_decode_shapes(cache, num_seqs, num_q_heads, 0, num_splits,

@@ -89,10 +89,4 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
                               int32_t num_pairs, int64_t block_vec16, int32_t num_blocks,
                               hipStream_t stream);
 
-// Streaming-read probe (measurement helper): reads n_vec16 16-byte words at
-// buf once; writes *sink only when a lane's XOR of its words equals
-// kReadProbeMagic.
-constexpr uint32_t kReadProbeMagic = 0x9E3779B9u;
-hipError_t launch_read_probe(const void* buf, int64_t n_vec16, uint32_t* sink, hipStream_t stream);
-
 }  // namespace pa

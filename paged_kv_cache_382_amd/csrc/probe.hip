@@ -12,10 +12,17 @@
 // stored only when it equals a fixed constant, so the loads cannot be dropped
 // and nothing is written in practice.
 
-#include "kernels.h"
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa_probe.h"
 
 namespace pa {
 namespace {
+
+// A lane writes the sink only when the XOR of its words equals this value.
+constexpr uint32_t kReadProbeMagic = 0x9E3779B9u;
 
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 constexpr int kProbeLanes = 256;
@@ -40,8 +47,6 @@ __global__ __launch_bounds__(kProbeLanes) void read_probe_kernel(const u4* __res
     if (acc == kReadProbeMagic) *sink = acc;
 }
 
-}  // namespace
-
 hipError_t launch_read_probe(const void* buf, int64_t n_vec16, uint32_t* sink, hipStream_t stream) {
     if (n_vec16 <= 0) return hipSuccess;
     constexpr int64_t kPerIter = static_cast<int64_t>(kProbeLanes) * kProbeUnroll;
@@ -53,4 +58,15 @@ hipError_t launch_read_probe(const void* buf, int64_t n_vec16, uint32_t* sink, h
     return hipGetLastError();
 }
 
+}  // namespace
 }  // namespace pa
+
+extern "C" pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream) {
+    if (bytes % 16 != 0) return PA_ERR_SHAPE;
+    if (bytes == 0) return PA_OK;
+    if (!buf || !sink) return PA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0) return PA_ERR_ALIGN;
+    const hipError_t err = pa::launch_read_probe(buf, static_cast<int64_t>(bytes / 16), sink,
+                                                 static_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}

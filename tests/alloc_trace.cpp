@@ -101,8 +101,8 @@ struct Trace {
                     die("a sequence reads another token", ids[static_cast<size_t>(i)], p);
             }
         }
-        pa_alloc_stats st;
-        if (pa_alloc_get_stats(a, &st) != PA_OK) die("stats");
+        pa_alloc_stats_t st;
+        if (pa_alloc_stats(a, &st) != PA_OK) die("stats");
         if (st.live_seqs != static_cast<int64_t>(live.size())) die("live count", st.live_seqs, live.size());
         if (st.free_blocks + st.used_blocks != nb) die("free + used", st.free_blocks, st.used_blocks);
         if (pa_alloc_num_free(a) != st.free_blocks) die("num_free");

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-import paged_kv_cache_382_amd as pa
+from paged_kv_cache_382_amd import probe as pa_probe
 from tests.gpu_problems import DEV, say
 
 pytestmark = pytest.mark.gpu
@@ -20,7 +20,7 @@ def probe(nbytes, plant_word=None):
         buf[plant_word] = int(MAGIC)
     sink = torch.zeros(1, dtype=torch.int32, device=DEV)
     say(f"read probe: {nbytes} bytes, planted word {plant_word}")
-    pa.pa_read_probe(buf, sink)
+    pa_probe.pa_read_probe(buf, sink)
     torch.cuda.synchronize()
     return int(sink.item())
 
