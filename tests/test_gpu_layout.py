@@ -103,20 +103,20 @@ def test_head_major_decode_equals_slot_major_and_oracle(case, num_splits):
     check_close(out_h, ref, "head-major decode")
 
 
-@pytest.mark.parametrize("g,bs", [(1, 16), (4, 16), (2, 8)])
-def test_head_major_prefill_equals_slot_major_and_oracle(g, bs):
-    hkv, d = 2, 128
+@pytest.mark.parametrize("g,bs,d", [(1, 16, 128), (4, 16, 128), (2, 8, 128), (8, 32, 64), (3, 64, 64)])
+def test_head_major_prefill_equals_slot_major_and_oracle(g, bs, d):
+    hkv = 2
     lens = [300, 77, 129]
     chunks = [100, 77, 33]
     nb = sum(-(-L // bs) for L in lens) + 8
-    kc, vc, tables, lens = problem(10 + g, nb, bs, hkv, d, lens)
+    kc, vc, tables, lens = problem(10 + g + d, nb, bs, hkv, d, lens)
     starts = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     q = W.normal_fp16((int(starts[-1]), hkv * g, d), 70 + g, DEV)
     t = torch.from_numpy(tables).to(DEV)
     ll = torch.tensor(lens, dtype=torch.int32, device=DEV)
     qs = torch.from_numpy(starts).to(DEV)
     scale = float(np.float32(1.0 / np.sqrt(d)))
-    say(f"prefill layouts g {g} bs {bs}")
+    say(f"prefill layouts g {g} bs {bs} d {d}")
     out_s = pa.pa_prefill(q, kc, vc, t, ll, qs, scale, max_query_len=max(chunks))
     kh, vh = head_major(kc), head_major(vc)
     out_h = pa.pa_prefill(q, kh, vh, t, ll, qs, scale, max_query_len=max(chunks), layout="head")
