@@ -273,8 +273,9 @@ int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads,
  *
  * head_dim 64 or 128; block_size a power of two; any group size.  Lengths are clamped
  * on the device so that nothing outside the buffers is read; a key behind an
- * out-of-range table entry takes its K row from slot 0 of the cache and a zero
- * V row (the result of rows that see it is then unspecified).  PA_VALIDATE
+ * out-of-range table entry takes a zero V row and a zero K row (block_size
+ * >= 16) or slot 0's K row (smaller blocks); the result of rows that see it
+ * is then unspecified.  PA_VALIDATE
  * checks all of this on the host first.  No
  * workspace; enqueued on hip_stream.
  */

@@ -19,11 +19,13 @@
 // heads become extra rows of one contraction and every K/V row read from HBM
 // serves all G heads.  A workgroup of kWaves waves owns 32*kNT*kWaves rows,
 // 32*kNT a wave.  For each tile of KT keys:
-//   * the workgroup stages K (row-major, rows padded to D*2+16 bytes) and V
-//     (transposed, [d][slot], slot = key with bits 2 and 3 swapped) in one of
-//     two LDS buffers; while tile t is consumed, tile t+1 is written to the
-//     other buffer, tile t+2's global loads are in flight and tile t+3's
-//     block ids are being fetched, so there is one barrier per tile;
+//   * the workgroup brings the tile's K and V rows into LDS: with blocks of
+//     16 tokens or more straight from HBM (prefill_lds_kernel, below: loads
+//     that write LDS, three stages, V in row order); with smaller blocks
+//     through registers (prefill_kernel: K rows padded to D*2+16 bytes, V
+//     transposed, [d][slot], slot = key with bits 2 and 3 swapped, two LDS
+//     buffers, tile t+2's loads in flight and tile t+3's block ids being
+//     fetched); one barrier per tile either way;
 //   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_f16 (A = K from
 //     LDS, B = Q held in registers), so that a lane owns one query row
 //     (column l % 32) and 16 keys of each 32-key sub-tile;
@@ -34,11 +36,15 @@
 //   * O^T += V^T P^T with the probabilities taken straight from the S^T
 //     accumulators as the B operand: accumulator register r of a 32-key
 //     sub-tile holds key (r/4)*8 + 4*(l/32) + r%4, which is MFMA k-slot
-//     8*(l/32) + r%8 of k-step r/8 once V's keys are stored in slot order.
-// Keys past the context or behind an out-of-range table entry read slot 0 of
-// the cache (a safe address) and their V rows are zeroed when staged; keys
-// past the context are also behind every row's causal limit, so their scores
-// are masked.
+//     8*(l/32) + r%8 of k-step r/8 once V's keys are read in that order
+//     (stored so in the register-staged kernel, picked so by the transposing
+//     reads in the other).
+// Keys past the context or behind an out-of-range table entry contribute no
+// value: their V rows are zero (the register-staged kernel reads slot 0 of the
+// cache for them, a safe address, and zeroes the V rows when staging; the
+// other loads them through a buffer range that ends before them); keys past
+// the context are also behind every row's causal limit, so their scores are
+// masked.
 // The output is normalised once and rounded to fp16 (round to nearest even).
 
 #include <type_traits>
