@@ -304,6 +304,34 @@ def read_ceiling(buffers, reps):
             "non-temporal loads, one contiguous range per workgroup)"}
 
 
+def mfma_ceiling(dev, reps):
+    """The fp16 matrix-core rate the device sustains: ``pa_mfma_probe`` with
+    two 8-wave workgroups per compute unit (all resident), ``reps`` launches
+    timed with HIP events; the median launch is reported, with the check that
+    every product ran (the probe's sink stays 0)."""
+    import torch
+
+    from paged_kv_cache_382_amd import probe
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 8192
+    probe.pa_mfma_probe(sink, wgs, iters)
+    torch.cuda.synchronize()
+    times, flops = [], 0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = probe.pa_mfma_probe(sink, wgs, iters)
+        e1.record()
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    rates = [flops / (a.elapsed_time(b) * 1e-3) / 1e12 for a, b in times]
+    return {"tflops": round(float(np.median(rates)), 2), "flops_per_launch": flops, "launches": reps,
+            "products_checked": int(sink.item()) == 0,
+            "kernel": (f"mfma_probe_kernel (pa_mfma_probe: {wgs} workgroups x 8 waves, four "
+                       "independent v_mfma_f32_32x32x16_f16 chains per wave)")}
+
+
 def copy_probe(wl, dev, reps):
     """Copy blocks [0, NB/2) onto [NB/2, NB) in both caches, ``reps`` times.
 
@@ -515,7 +543,7 @@ def prefill_main(args, wl, dev):
         "prefill_us_percentiles": pcts([x * 1e3 for x in pf_each]),
         "roofline": {
             "bound": "mfma",
-            "kernel": "pa_prefill (prefill_kernel)",
+            "kernel": "pa_prefill ({})".format("prefill_lds_kernel" if bs >= 16 else "prefill_kernel"),
             "achieved": round(achieved, 2),
             "peak": PEAK_FP16_TFLOPS,
             "unit": "TFLOP/s",
@@ -525,6 +553,10 @@ def prefill_main(args, wl, dev):
             "algorithmic_bytes_per_launch": prefill_kv_bytes(lens, hkv, d) + 2 * T * hq * d * 2,
         },
     }
+    if not args.no_mfma_ceiling:
+        ceiling = mfma_ceiling(dev, 5)
+        result["mfma_ceiling"] = ceiling
+        result["roofline"]["frac_of_mfma_ceiling"] = round(achieved / ceiling["tflops"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = prefill_cpu_baseline(wl, caches[0][0], caches[0][1], q[0],
                                                       tables_h, lens_h, chunk, args.cpu_budget,
@@ -801,6 +833,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read probe on layer 0's caches")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="prefill: skip timing the matrix-core probe")
     ap.add_argument("--no-mix", dest="with_mix", action="store_false",
                     help="with the default mha workload, skip the second measured configuration "
                          "(mixed context lengths, reported under 'mix')")

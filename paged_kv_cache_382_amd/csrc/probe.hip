@@ -1,16 +1,27 @@
-// Streaming-read probe: a measurement helper, not a step of the attention path.
+// Measurement probes: helpers beside the attention path, not steps of it.
 //
-// The pages tie decode speed to memory bandwidth ("vLLM core architecture
-// ...", section 3, "Continuous batching").  This kernel reads a device buffer
-// once, as fast as the device streams reads, so that the decode kernel's
-// bandwidth can be set beside what the same device reaches with nothing but
-// reads, on the same buffer, in the same run.
-//
+// Streaming-read probe.  The pages tie decode speed to memory bandwidth
+// ("vLLM core architecture ...", section 3, "Continuous batching").  This
+// kernel reads a device buffer once, as fast as the device streams reads, so
+// that the decode kernel's bandwidth can be set beside what the same device
+// reaches with nothing but reads, on the same buffer, in the same run.
 // Design: the buffer is cut into equal contiguous ranges, one per workgroup
 // (at most 4096 of them, 256 lanes each); every lane keeps 16 non-temporal
 // 16-byte loads in flight.  The words are folded with XOR and the result is
 // stored only when it equals a fixed constant, so the loads cannot be dropped
 // and nothing is written in practice.
+//
+// Matrix-core probe.  Chunked prefill is a dense contraction on the matrix
+// cores ("Deep dive into the nano-vLLM inference engine architecture:
+// PagedAttention memory management", section "Deployable configuration
+// parameters": prompts are prefilled in chunks).  This kernel issues the
+// prefill kernel's fp16 matrix instruction back to back with nothing else to
+// do, so that the prefill kernel's rate can be set beside what the same device
+// sustains, at the clock it holds under matrix load, in the same run.  Each
+// wave keeps four independent accumulation chains of v_mfma_f32_32x32x16_f16
+// on register operands; every operand is the caller's value, so each product
+// adds 16 * operand^2 to every accumulator, which the kernel checks exactly at
+// the end.
 
 #include <hip/hip_runtime.h>
 
@@ -58,6 +69,40 @@ hipError_t launch_read_probe(const void* buf, int64_t n_vec16, uint32_t* sink, h
     return hipGetLastError();
 }
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16x __attribute__((ext_vector_type(16)));
+constexpr int kMfmaLanes = 512;                  // 8 waves: two per SIMD
+constexpr int kMfmaChains = 4;
+
+__global__ __launch_bounds__(kMfmaLanes) void mfma_probe_kernel(int32_t iters, float operand, uint32_t* sink) {
+    h8 a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = static_cast<_Float16>(operand);
+    f16x c[kMfmaChains];
+#pragma unroll
+    for (int k = 0; k < kMfmaChains; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[k][r] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < kMfmaChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c[k], 0, 0, 0);
+    }
+    // Operand 1: every accumulator holds 16 * iters exactly (iters <= 65536).
+    const float want = 16.0f * static_cast<float>(iters);
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < kMfmaChains; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ok = ok && c[k][r] == want;
+    if (!ok) *sink = 1u;
+}
+
+hipError_t launch_mfma_probe(uint32_t* sink, int32_t workgroups, int32_t iters, float operand, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(kMfmaLanes), 0, stream,
+                       iters, operand, sink);
+    return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -68,5 +113,15 @@ extern "C" pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink
     if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0) return PA_ERR_ALIGN;
     const hipError_t err = pa::launch_read_probe(buf, static_cast<int64_t>(bytes / 16), sink,
                                                  static_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_mfma_probe(uint32_t* sink, int32_t workgroups, int32_t iters, float operand,
+                                   void* hip_stream) {
+    if (workgroups < 0 || workgroups > 65536 || iters < 1 || iters > 65536) return PA_ERR_SHAPE;
+    if (workgroups == 0) return PA_OK;
+    if (!sink) return PA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return PA_ERR_ALIGN;
+    const hipError_t err = pa::launch_mfma_probe(sink, workgroups, iters, operand, static_cast<hipStream_t>(hip_stream));
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

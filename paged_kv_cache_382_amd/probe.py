@@ -1,5 +1,6 @@
 """ctypes binding of ``lib/libpa_probe.so`` (include/pa_probe.h): the
-streaming-read probe, a measurement helper beside the attention library."""
+streaming-read and matrix-core probes, measurement helpers beside the
+attention library."""
 
 import ctypes
 import os
@@ -11,7 +12,13 @@ PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
 # name -> (restype, argtypes): every symbol declared in include/pa_probe.h
 SIGNATURES = {
     "pa_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "pa_mfma_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                     ctypes.c_void_p]),
 }
+
+# Work of one pa_mfma_probe call per workgroup and iteration: 8 waves, four
+# 32 x 32 x 16 products each (2 * 32 * 32 * 16 flops a product).
+MFMA_PROBE_FLOPS_PER_WG_ITER = 8 * 4 * 2 * 32 * 32 * 16
 
 _lib = None
 
@@ -43,3 +50,16 @@ def pa_read_probe(buf, sink, stream=None):
                                  _dev(sink, torch.int32, "sink"), _stream(stream))
     if status != 0:
         raise PaError(status, "pa_read_probe failed")
+
+
+def pa_mfma_probe(sink, workgroups, iters, operand=1.0, stream=None):
+    """Run ``workgroups`` x 8 waves of back-to-back fp16 matrix products
+    (``iters`` iterations of four independent chains per wave); ``sink`` is a
+    one-element int32 device tensor, set to 1 if any accumulator differs from
+    its value for ``operand`` 1.0.  Returns the flops of the call."""
+    import torch
+    status = lib().pa_mfma_probe(_dev(sink, torch.int32, "sink"), int(workgroups), int(iters),
+                                 float(operand), _stream(stream))
+    if status != 0:
+        raise PaError(status, "pa_mfma_probe failed")
+    return int(workgroups) * int(iters) * MFMA_PROBE_FLOPS_PER_WG_ITER

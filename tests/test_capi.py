@@ -38,14 +38,15 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_probe_library_exports_its_header_and_stays_out_of_the_path():
-    """The streaming-read probe is a library of its own (include/pa_probe.h);
-    the attention library does not export it."""
+    """The measurement probes are a library of their own (include/pa_probe.h);
+    the attention library exports neither."""
     probe_names = declared_functions(PROBE_HEADER)
-    assert probe_names == ["pa_read_probe"]
+    assert probe_names == ["pa_mfma_probe", "pa_read_probe"]
     handle = ctypes.CDLL(pa_probe.PROBE_LIB_PATH)
     assert all(hasattr(handle, n) for n in probe_names)
     assert set(probe_names) == set(pa_probe.SIGNATURES)
-    assert not hasattr(ctypes.CDLL(pa.LIB_PATH), "pa_read_probe")
+    attention = ctypes.CDLL(pa.LIB_PATH)
+    assert not any(hasattr(attention, n) for n in probe_names)
 
 
 @pytest.mark.parametrize("buf,nbytes,sink,code", [
@@ -61,6 +62,22 @@ def test_read_probe_rejects_bad_arguments(buf, nbytes, sink, code):
 
 def test_read_probe_of_nothing_launches_nothing():
     assert pa_probe.lib().pa_read_probe(None, 0, None, None) == 0
+
+
+@pytest.mark.parametrize("sink,workgroups,iters,code", [
+    (0x2000, -1, 8, "SHAPE"),
+    (0x2000, 65537, 8, "SHAPE"),
+    (0x2000, 4, 0, "SHAPE"),
+    (0x2000, 4, 65537, "SHAPE"),
+    (None, 4, 8, "NULL"),
+    (0x2002, 4, 8, "ALIGN"),
+])
+def test_mfma_probe_rejects_bad_arguments(sink, workgroups, iters, code):
+    assert pa_probe.lib().pa_mfma_probe(sink, workgroups, iters, 1.0, None) == NAMES[code]
+
+
+def test_mfma_probe_of_no_workgroups_launches_nothing():
+    assert pa_probe.lib().pa_mfma_probe(None, 0, 8, 1.0, None) == 0
 
 
 def _desc(nb=64, bs=16, hkv=4, d=64):

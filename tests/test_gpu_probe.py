@@ -1,6 +1,9 @@
-"""The streaming-read probe (a measurement helper) reads every 16-byte word of
-its buffer: a lane's XOR of the words it read reaches the sink constant only
-when the one planted word is read (an odd number of times) by that lane."""
+"""The measurement probes.  The streaming-read probe reads every 16-byte word
+of its buffer: a lane's XOR of the words it read reaches the sink constant
+only when the one planted word is read (an odd number of times) by that lane.
+The matrix-core probe runs every product it counts: with operand 1 each of
+its accumulators ends at exactly 16 per iteration (the sink stays 0), with
+operand 2 at four times that (the sink is set)."""
 
 import numpy as np
 import pytest
@@ -41,3 +44,17 @@ def test_planted_word_is_read(nbytes, where):
     w = {"first": 0, "last": words - 1,
          "random": int(np.random.default_rng(7).integers(0, words))}[where]
     assert probe(nbytes, w) == int(MAGIC)
+
+
+@pytest.mark.parametrize("workgroups,iters", [(1, 1), (3, 17), (512, 256)])
+def test_mfma_probe_runs_every_product(workgroups, iters):
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say(f"mfma probe: {workgroups} workgroups, {iters} iterations, operand 1")
+    flops = pa_probe.pa_mfma_probe(sink, workgroups, iters, 1.0)
+    torch.cuda.synchronize()
+    assert flops == workgroups * iters * 8 * 4 * 32768
+    assert int(sink.item()) == 0
+    say(f"mfma probe: {workgroups} workgroups, {iters} iterations, operand 2")
+    pa_probe.pa_mfma_probe(sink, workgroups, iters, 2.0)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 1
