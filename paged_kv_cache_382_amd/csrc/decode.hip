@@ -19,8 +19,10 @@
 //   out[s][h] = sum_p softmax_p(scale * q[s][h] . K[s,p,g]) V[s,p,g]
 // with K/V row p found in physical block table[s][p / BS], row p % BS.
 //
-// Design (HBM-bound streaming; no matrix cores: G <= 8 query rows never fill
-// an MFMA tile):
+// Design (HBM-bound streaming).  This vector kernel (decode_split_kernel)
+// serves 1 or 2 query heads per KV head and block size 8; 3 to 8 query heads
+// per KV head run the same partition on the matrix cores (decode_mfma_kernel,
+// below), and larger groups are cut into virtual KV heads of at most 8:
 //  * Short contexts (a bound of at most 512 tokens, at most 64 sequences):
 //    workgroup w takes (sequence, KV head) pair w whole and writes its fp16
 //    rows; no merge kernel runs.  One launch instead of two where launch
@@ -80,9 +82,10 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kChunk = 16;         // tokens per chunk
-// Occupancy (waves per SIMD) the register allocator may trade down to while
-// keeping two chunks of K and V in registers: 4 waves (128 VGPRs) for 1-2
-// query heads per KV head, 3 (168) for 4, 2 (256) for 8.
+// Occupancy (waves per SIMD) the register allocator of the vector kernel may
+// trade down to while keeping two chunks of K and V in registers: 4 waves (128
+// VGPRs) for 1-2 query heads per KV head, 3 (168) for 4, 2 (256) for the other
+// groups (which reach this kernel only with blocks of 8 tokens).
 template <int G>
 constexpr int waves_per_simd() { return G <= 2 ? 4 : (G == 4 ? 3 : 2); }
 constexpr float kNegBig = -1.0e30f;  // start value of a running max
