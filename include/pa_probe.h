@@ -16,6 +16,13 @@
  * matrix instruction back to back with nothing else, so that the prefill
  * kernel's rate can be set beside what the device sustains, at the clock it
  * holds under matrix load, in the same run.
+ *
+ * pa_range_probe -- not a measurement but a check of the hardware behaviour
+ * the attention kernels rely on (include/pa.h: rows behind a buffer range
+ * that ends at a context's last token, or behind an out-of-range table entry,
+ * contribute zeros): a 16-byte buffer load, into registers and into LDS,
+ * returns zeros for the dwords at or past the resource's range, with the
+ * range check covering the scalar offset as well as the lane offset.
  */
 #ifndef PA_PROBE_H
 #define PA_PROBE_H
@@ -56,6 +63,23 @@ pa_status pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip
  * launch.  Errors: PA_ERR_SHAPE (counts out of range), PA_ERR_NULL,
  * PA_ERR_ALIGN, PA_ERR_HIP (launch failed). */
 pa_status pa_mfma_probe(uint32_t* sink, int32_t workgroups, int32_t iters, float operand, void* hip_stream);
+
+/*   buf          device, 16-byte aligned, alloc_bytes bytes allocated
+ *   range_bytes  the buffer resource's range (<= alloc_bytes)
+ *   soffset      the scalar offset added to every lane's offset (multiple of 4)
+ *   voffsets     HOST array of n lane offsets (multiples of 4), each with
+ *                voffset + soffset + 16 <= alloc_bytes, so no load can leave
+ *                the allocation whatever the range check does
+ *   n            1 .. 64 lanes
+ *   out          device uint32 [2][n][4]: out[0][j] the 16 bytes lane j's
+ *                register load returned, out[1][j] the 16 bytes its
+ *                LDS-writing load put in LDS (dwords past the range: 0)
+ *
+ * One workgroup of 64 lanes; enqueued on hip_stream, returns after the launch.
+ * Errors: PA_ERR_SHAPE (n), PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_RANGE (range or
+ * an offset beyond the allocation), PA_ERR_HIP. */
+pa_status pa_range_probe(const void* buf, size_t alloc_bytes, uint32_t range_bytes, uint32_t soffset,
+                         const uint32_t* voffsets, int32_t n, uint32_t* out, void* hip_stream);
 
 #ifdef __cplusplus
 }

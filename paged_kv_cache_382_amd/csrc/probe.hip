@@ -22,6 +22,15 @@
 // on register operands; every operand is the caller's value, so each product
 // adds 16 * operand^2 to every accumulator, which the kernel checks exactly at
 // the end.
+//
+// Buffer range probe.  The decode and prefill kernels read the cache through
+// buffer resources whose range ends at the last row that holds a token (the
+// ragged last chunk of a context, the keys a prefill workgroup sees, an
+// out-of-range table entry): the rows behind the end must arrive as zeros,
+// both for loads into registers and for loads that write LDS directly, and
+// the check must cover the scalar offset that the kernels add to every lane's
+// offset.  This kernel makes exactly those loads over a caller's buffer, so
+// that a test can pin the behaviour the kernels rely on.
 
 #include <hip/hip_runtime.h>
 
@@ -71,6 +80,7 @@ hipError_t launch_read_probe(const void* buf, int64_t n_vec16, uint32_t* sink, h
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16x __attribute__((ext_vector_type(16)));
+constexpr int kRangeProbeLanes = 64;
 constexpr int kMfmaLanes = 512;                  // 8 waves: two per SIMD
 constexpr int kMfmaChains = 4;
 
@@ -103,6 +113,44 @@ hipError_t launch_mfma_probe(uint32_t* sink, int32_t workgroups, int32_t iters, 
     return hipGetLastError();
 }
 
+constexpr int kRsrcWord3 = 0x00020000;          // 32-bit data format, no swizzle
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct RangeProbeArgs {
+    const void* buf;
+    uint32_t range;
+    uint32_t soffset;
+    int32_t n;
+    uint32_t voff[kRangeProbeLanes];
+    uint32_t* out;
+};
+
+__global__ __launch_bounds__(kRangeProbeLanes) void range_probe_kernel(RangeProbeArgs a) {
+    __shared__ __align__(16) uint32_t tile[kRangeProbeLanes * 4];
+    const int j = threadIdx.x;
+    // Lanes past n repeat lane 0's offset (every offset was checked against
+    // the allocation) and store nothing.
+    const uint32_t v = a.voff[j < a.n ? j : 0];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.buf), 0,
+                                                                        static_cast<int>(a.range), kRsrcWord3);
+    const u4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, v, a.soffset, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)tile, 16, v, a.soffset, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): the LDS writes have landed
+    __syncthreads();
+    if (j < a.n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a.out[j * 4 + i] = r[i];
+            a.out[(a.n + j) * 4 + i] = tile[j * 4 + i];
+        }
+    }
+}
+
+hipError_t launch_range_probe(const RangeProbeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(range_probe_kernel, dim3(1), dim3(kRangeProbeLanes), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -123,5 +171,28 @@ extern "C" pa_status pa_mfma_probe(uint32_t* sink, int32_t workgroups, int32_t i
     if (!sink) return PA_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return PA_ERR_ALIGN;
     const hipError_t err = pa::launch_mfma_probe(sink, workgroups, iters, operand, static_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_range_probe(const void* buf, size_t alloc_bytes, uint32_t range_bytes, uint32_t soffset,
+                                    const uint32_t* voffsets, int32_t n, uint32_t* out, void* hip_stream) {
+    if (n < 1 || n > pa::kRangeProbeLanes) return PA_ERR_SHAPE;
+    if (!buf || !voffsets || !out) return PA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0 || soffset % 4 != 0)
+        return PA_ERR_ALIGN;
+    if (range_bytes > alloc_bytes) return PA_ERR_RANGE;
+    pa::RangeProbeArgs a{};
+    for (int j = 0; j < n; ++j) {
+        if (voffsets[j] % 4 != 0) return PA_ERR_ALIGN;
+        // Every load stays inside the allocation even without a range check.
+        if (static_cast<uint64_t>(voffsets[j]) + soffset + 16 > alloc_bytes) return PA_ERR_RANGE;
+        a.voff[j] = voffsets[j];
+    }
+    a.buf = buf;
+    a.range = range_bytes;
+    a.soffset = soffset;
+    a.n = n;
+    a.out = out;
+    const hipError_t err = pa::launch_range_probe(a, static_cast<hipStream_t>(hip_stream));
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -1,6 +1,7 @@
 """ctypes binding of ``lib/libpa_probe.so`` (include/pa_probe.h): the
-streaming-read and matrix-core probes, measurement helpers beside the
-attention library."""
+streaming-read and matrix-core probes (measurement helpers beside the
+attention library) and the buffer range probe (a check of the hardware
+behaviour the attention kernels rely on)."""
 
 import ctypes
 import os
@@ -14,6 +15,9 @@ SIGNATURES = {
     "pa_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "pa_mfma_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                      ctypes.c_void_p]),
+    "pa_range_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_uint32,
+                                      ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
 }
 
 # Work of one pa_mfma_probe call per workgroup and iteration: 8 waves, four
@@ -63,3 +67,23 @@ def pa_mfma_probe(sink, workgroups, iters, operand=1.0, stream=None):
     if status != 0:
         raise PaError(status, "pa_mfma_probe failed")
     return int(workgroups) * int(iters) * MFMA_PROBE_FLOPS_PER_WG_ITER
+
+
+def pa_range_probe(buf, range_bytes, soffset, voffsets, out, stream=None):
+    """16-byte buffer loads from the contiguous device tensor ``buf`` through a
+    resource of ``range_bytes``, at lane offsets ``voffsets`` (a list of at most
+    64) plus the scalar offset ``soffset``; ``out`` (int32 device tensor of
+    2 * len(voffsets) * 4 elements) receives what each lane's register load
+    returned, then what its LDS-writing load put in LDS."""
+    import torch
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    n = len(voffsets)
+    if out.numel() != 2 * n * 4:
+        raise ValueError("out must hold 2 * len(voffsets) * 4 int32 values")
+    arr = (ctypes.c_uint32 * max(n, 1))(*[int(v) for v in voffsets])
+    status = lib().pa_range_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                  int(range_bytes), int(soffset), arr, n, _dev(out, torch.int32, "out"),
+                                  _stream(stream))
+    if status != 0:
+        raise PaError(status, "pa_range_probe failed")

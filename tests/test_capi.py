@@ -41,7 +41,7 @@ def test_probe_library_exports_its_header_and_stays_out_of_the_path():
     """The measurement probes are a library of their own (include/pa_probe.h);
     the attention library exports neither."""
     probe_names = declared_functions(PROBE_HEADER)
-    assert probe_names == ["pa_mfma_probe", "pa_read_probe"]
+    assert probe_names == ["pa_mfma_probe", "pa_range_probe", "pa_read_probe"]
     handle = ctypes.CDLL(pa_probe.PROBE_LIB_PATH)
     assert all(hasattr(handle, n) for n in probe_names)
     assert set(probe_names) == set(pa_probe.SIGNATURES)
@@ -78,6 +78,28 @@ def test_mfma_probe_rejects_bad_arguments(sink, workgroups, iters, code):
 
 def test_mfma_probe_of_no_workgroups_launches_nothing():
     assert pa_probe.lib().pa_mfma_probe(None, 0, 8, 1.0, None) == 0
+
+
+def _offsets(*vals):
+    return (ctypes.c_uint32 * len(vals))(*vals)
+
+
+@pytest.mark.parametrize("buf,alloc,rng,soff,offs,n,out,code", [
+    (0x1000, 4096, 4096, 0, (0,), 0, 0x2000, "SHAPE"),          # no lanes
+    (0x1000, 4096, 4096, 0, (0,) * 65, 65, 0x2000, "SHAPE"),    # more than 64 lanes
+    (None, 4096, 4096, 0, (0,), 1, 0x2000, "NULL"),
+    (0x1000, 4096, 4096, 0, None, 1, 0x2000, "NULL"),
+    (0x1000, 4096, 4096, 0, (0,), 1, None, "NULL"),
+    (0x1008, 4096, 4096, 0, (0,), 1, 0x2000, "ALIGN"),          # buf not 16-byte aligned
+    (0x1000, 4096, 4096, 2, (0,), 1, 0x2000, "ALIGN"),          # soffset not a multiple of 4
+    (0x1000, 4096, 4096, 0, (6,), 1, 0x2000, "ALIGN"),          # voffset not a multiple of 4
+    (0x1000, 4096, 4097, 0, (0,), 1, 0x2000, "RANGE"),          # range past the allocation
+    (0x1000, 4096, 4096, 0, (4084,), 1, 0x2000, "RANGE"),       # a load could leave the allocation
+    (0x1000, 4096, 4096, 16, (4072,), 1, 0x2000, "RANGE"),      # ... once soffset is added
+])
+def test_range_probe_rejects_bad_arguments(buf, alloc, rng, soff, offs, n, out, code):
+    arr = _offsets(*offs) if offs is not None else None
+    assert pa_probe.lib().pa_range_probe(buf, alloc, rng, soff, arr, n, out, None) == NAMES[code]
 
 
 def _desc(nb=64, bs=16, hkv=4, d=64):

@@ -3,7 +3,10 @@ of its buffer: a lane's XOR of the words it read reaches the sink constant
 only when the one planted word is read (an odd number of times) by that lane.
 The matrix-core probe runs every product it counts: with operand 1 each of
 its accumulators ends at exactly 16 per iteration (the sink stays 0), with
-operand 2 at four times that (the sink is set)."""
+operand 2 at four times that (the sink is set).  The buffer range probe pins
+the hardware behaviour the attention kernels rely on: 16-byte buffer loads,
+into registers and into LDS, return zeros at and past the resource's range,
+with the scalar offset counted."""
 
 import numpy as np
 import pytest
@@ -58,3 +61,28 @@ def test_mfma_probe_runs_every_product(workgroups, iters):
     pa_probe.pa_mfma_probe(sink, workgroups, iters, 2.0)
     torch.cuda.synchronize()
     assert int(sink.item()) == 1
+
+
+@pytest.mark.parametrize("range_bytes", [4096, 4096 + 256, 256 * 37])
+@pytest.mark.parametrize("soffset", [0, 256, 2048, 4096])
+def test_range_check_covers_the_scalar_offset(range_bytes, soffset):
+    """Every dword at byte range_bytes or beyond (lane offset plus scalar
+    offset) reads as zero; every dword before it reads the buffer.  The lane
+    offsets are 16-byte aligned and the ranges whole rows of 256 bytes, as in
+    the kernels, so no load straddles the end."""
+    alloc = 16384
+    words = torch.arange(1, alloc // 4 + 1, dtype=torch.int32, device=DEV)    # word w holds w + 1
+    voffsets = [0, 16, 240, 256, 1024, 2032, 2048, 3824, 3840, 4080, 4096, 4352, 5120,
+                6144, 8176, 9456, 9472, 12288 - 16]
+    voffsets = [v for v in voffsets if v + soffset + 16 <= alloc]
+    out = torch.full((2, len(voffsets), 4), -7, dtype=torch.int32, device=DEV)
+    say(f"range probe: range {range_bytes}, soffset {soffset}, {len(voffsets)} lanes")
+    pa_probe.pa_range_probe(words, range_bytes, soffset, voffsets, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for j, v in enumerate(voffsets):
+        for i in range(4):
+            addr = v + soffset + 4 * i
+            want = addr // 4 + 1 if addr < range_bytes else 0
+            assert got[0, j, i] == want, ("register load", v, soffset, i)
+            assert got[1, j, i] == want, ("LDS load", v, soffset, i)
