@@ -186,7 +186,14 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  *                  bytes (same cache, num_seqs, num_q_heads, num_splits, on
  *                  the same device), 256-byte aligned, for those partials.
  *                  Its contents on entry do not matter; calls sharing a
- *                  workspace must not overlap.
+ *                  workspace must not overlap.  Where it applies (slot-major
+ *                  layout, groups of 3 to 8 query heads, block_size >= 16, a
+ *                  multiple of 4 KV heads), pa_decode_workspace_bytes reports
+ *                  the size of the head-group order, in which the 4 waves of a
+ *                  workgroup read the same tokens of 4 adjacent KV heads;
+ *                  pa_decode takes that order whenever workspace_bytes holds
+ *                  it, and the plain order (N + num_seqs * num_kv_heads slots)
+ *                  otherwise.
  *
  * Supported: head_dim 64 or 128; block_size 8, 16, 32 or 64; num_q_heads any
  * multiple of num_kv_heads.  A group G = num_q_heads / num_kv_heads of up to 8
@@ -194,10 +201,11 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  * block_size >= 16); a larger group runs as G / g groups of its largest
  * divisor g <= 8, each reading its KV head's rows again (the workspace and
  * the split count then cover num_kv_heads * G / g pairs per sequence).  Other
- * shapes return PA_ERR_UNSUPPORTED.  Results depend only on the context lengths and
- * N, never on which physical blocks hold the tokens or on which workgroup
- * handled which range: moving blocks (and rewriting the tables to match)
- * gives bitwise identical output.
+ * shapes return PA_ERR_UNSUPPORTED.  Results depend only on the context lengths,
+ * N and the order (head groups or plain, fixed by the shapes and whether the
+ * workspace holds the head-group order), never on which physical blocks hold
+ * the tokens or on which workgroup handled which range: moving blocks (and
+ * rewriting the tables to match) gives bitwise identical output.
  */
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const pa_cache_desc* cache,
@@ -214,7 +222,9 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * until the process ends; the call allocates
  * nothing (no hipMalloc, no host allocation) and does not apply validation
  * mode.  Arguments, layouts and results as pa_decode (same kernels, bitwise
- * the same output for the same num_splits).
+ * the same output for the same num_splits as pa_decode with a workspace of
+ * pa_decode_workspace_bytes, whenever the head-group order's partials fit the
+ * array; larger calls that still fit in the plain order run that order).
  *
  * Errors: PA_ERR_WORKSPACE, before any launch, when the call's partial
  * results need more than the scratch holds (workspace formula as
@@ -228,10 +238,13 @@ pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_ca
                             int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                             float scale, void* out, int32_t num_splits, void* hip_stream);
 
-/* Bytes of workspace pa_decode needs: (N + num_seqs * num_kv_heads) slots of
- * G x (head_dim + 2) floats, with G = num_q_heads / num_kv_heads and N the
- * resolved num_splits, each of the two arrays rounded up to 256 bytes.
- * Returns 0 for unsupported or invalid shapes. */
+/* Bytes of workspace pa_decode needs for its faster order: (N + num_seqs *
+ * num_kv_heads) slots of G x (head_dim + 2) floats, with G = num_q_heads /
+ * num_kv_heads and N the resolved num_splits, each of the two arrays rounded
+ * up to 256 bytes; (4N + num_seqs * num_kv_heads) slots where the head-group
+ * order applies (slot-major layout, groups of 3 to 8 query heads, block_size
+ * >= 16, a multiple of 4 KV heads; a larger group counts its virtual KV
+ * heads).  Returns 0 for unsupported or invalid shapes. */
 size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t num_splits);
 

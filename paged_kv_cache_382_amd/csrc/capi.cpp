@@ -93,19 +93,31 @@ constexpr int32_t kWholePairs = -1;
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Partial-result slots: one per split plus one per (sequence, KV head) pair
-// (virtual KV heads for a large query group), each of `group` rows.
-size_t partial_rows(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads, int32_t splits) {
+// Whether decode orders each sequence's chunk list by groups of 4 (virtual)
+// KV heads: the matrix-core kernel with a multiple of 4 virtual KV heads, on
+// the slot-major layout, where the 4 waves of a workgroup then read 1 KiB of
+// each token row together (head-major blocks already hold a head's rows
+// contiguously, and there the plain order measured faster).
+bool head_groups_ok(const pa_cache_desc* c, int32_t num_q_heads) {
     const GroupSplit gs = group_split(c, num_q_heads);
-    const size_t slots = static_cast<size_t>(splits) +
+    return c->layout == PA_LAYOUT_SLOT_MAJOR &&
+           decode_head_groups_ok(c->block_size, gs.group, c->num_kv_heads * gs.kv_split);
+}
+
+// Partial-result slots: one per split plus one per (sequence, KV head) pair
+// (virtual KV heads for a large query group), each of `group` rows; in the
+// head-group order four per split plus one per pair.
+size_t partial_rows(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads, int32_t splits, bool hg) {
+    const GroupSplit gs = group_split(c, num_q_heads);
+    const size_t slots = static_cast<size_t>(splits) * (hg ? 4 : 1) +
                          static_cast<size_t>(num_seqs) * c->num_kv_heads * gs.kv_split;
     return slots * static_cast<size_t>(gs.group);
 }
 
 // Workspace layout: part_ml fp32 [slots][G][2], then part_o fp32
 // [slots][G][D], each 256-byte aligned.
-size_t workspace_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads, int32_t splits) {
-    const size_t rows = partial_rows(c, num_seqs, num_q_heads, splits);
+size_t workspace_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads, int32_t splits, bool hg) {
+    const size_t rows = partial_rows(c, num_seqs, num_q_heads, splits, hg);
     return round_up(rows * 2 * sizeof(float)) + round_up(rows * c->head_dim * sizeof(float));
 }
 
@@ -196,7 +208,12 @@ pa_status decode_call(const char* fn, const void* q, const void* k_cache, const 
                                         ((max_tokens64 + 15) / 16);
             splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, chunk_bound)));
         }
-        const size_t need = workspace_for(cache, num_seqs, num_q_heads, splits);
+        // The plain order needs `need`; the head-group order (faster, when the
+        // kernel allows it) needs `need_hg` and is used whenever the
+        // workspace holds it.
+        const bool hg_ok = head_groups_ok(cache, num_q_heads);
+        const size_t need = workspace_for(cache, num_seqs, num_q_heads, splits, false);
+        const size_t need_hg = hg_ok ? workspace_for(cache, num_seqs, num_q_heads, splits, true) : need;
         if (scratch_ws) {
             // The library's own array: checked for size before the device
             // address is looked up (every argument check precedes it).
@@ -208,9 +225,11 @@ pa_status decode_call(const char* fn, const void* q, const void* k_cache, const 
             if (sst != PA_OK) return sst;
             workspace_bytes = kScratchBytes;
         }
-        if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need_hg);
         if (workspace_bytes < need)
-            return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn, workspace_bytes, need);
+            return fail(PA_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required (%zu for the faster order)",
+                        fn, workspace_bytes, need, need_hg);
+        const bool hg = hg_ok && workspace_bytes >= need_hg;
         if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
             return fail(PA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
         const GroupSplit gsplit = group_split(cache, num_q_heads);
@@ -244,7 +263,7 @@ pa_status decode_call(const char* fn, const void* q, const void* k_cache, const 
         a.context_lens = context_lens;
         a.out = static_cast<uint16_t*>(out);
         {
-            const size_t rows = partial_rows(cache, num_seqs, num_q_heads, splits);
+            const size_t rows = partial_rows(cache, num_seqs, num_q_heads, splits, hg);
             char* ws = static_cast<char*>(workspace);
             a.part_ml = reinterpret_cast<float*>(ws);
             a.part_o = reinterpret_cast<float*>(ws + round_up(rows * 2 * sizeof(float)));
@@ -261,6 +280,7 @@ pa_status decode_call(const char* fn, const void* q, const void* k_cache, const 
         a.scale_log2 = scale * kLog2e;
         a.head_major = cache->layout == PA_LAYOUT_HEAD_MAJOR;
         a.kv_split = gsplit.kv_split;
+        a.head_groups = hg ? 1 : 0;
         a.whole_pairs = 0;
         if (num_splits == kWholePairs && num_seqs > 64)
             return fail(PA_ERR_RANGE, "%s: num_splits -1 (whole pairs) takes at most 64 sequences", fn);
@@ -373,7 +393,8 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* cache, int32_t num_seqs, i
                                 "pa_decode_workspace_bytes") != PA_OK)
         return 0;
     return pa::workspace_for(cache, num_seqs, num_q_heads,
-                             pa::resolve_splits(cache, num_q_heads, num_splits));
+                             pa::resolve_splits(cache, num_q_heads, num_splits),
+                             pa::head_groups_ok(cache, num_q_heads));
 }
 
 int32_t pa_decode_num_splits(const pa_cache_desc* cache, int32_t num_q_heads, int32_t num_splits) {

@@ -679,10 +679,10 @@ __device__ __forceinline__ float tok_sum(float x) {
     return a + b;
 }
 
-// Register budget: 4 waves a SIMD (128 VGPRs) for G = 4, 3 for G = 3 (whose
-// 128-register form spills), 2 for G = 5..8.
+// Register budget: 3 waves a SIMD (168 VGPRs) for G = 3 and 4, whose 128-register
+// forms spill (the split count puts 3 workgroups on a CU anyway), 2 for G = 5..8.
 template <int G>
-constexpr int mfma_waves_per_simd() { return G == 4 ? 4 : (G == 3 ? 3 : 2); }
+constexpr int mfma_waves_per_simd() { return G <= 4 ? 3 : 2; }
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<G>())))
@@ -734,6 +734,21 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int len_reg = (lens_in_regs && lane < a.num_seqs) ? clamped_len(a, lane) : 0;
     const int64_t incl_reg = wave_incl_scan64(chunks_of(len_reg), lane);
     const int64_t U = (lens_in_regs ? readlane64(incl_reg, kWave - 1) : chunks_per_head(a, lane)) * Hkv;
+    // Head groups: a sequence's part of the list may run group by group of 4
+    // (virtual) KV heads, chunk-major inside a group with the group's heads
+    // interleaved (entry 4c + j: chunk c of head 4*hg + j).  Each wave then
+    // keeps one head for a whole segment, and the 4 waves of a workgroup read
+    // the same 16 tokens of 4 adjacent heads (1 KiB of each slot-major token
+    // row instead of 256-byte pieces 2 KiB apart).  Allowed with at least 4
+    // entries a split (every split that touches a head's entries then holds
+    // one of them), never for whole pairs; taken by a sequence whose groups
+    // span at most about 32 splits (seq_hg), so that the merge still reads
+    // each pair's partials in one round.  With head groups allowed, every
+    // partial slot is 4 * (split + group) + head in group, in either order.
+    const bool hg_mode = a.head_groups && !a.whole_pairs && U >= 4 * static_cast<int64_t>(N);
+    auto seq_hg = [&](int nch) {
+        return hg_mode && 4 * static_cast<int64_t>(nch) * N <= 30 * U;
+    };
     auto len_of = [&](int sq) {
         return lens_in_regs ? __builtin_amdgcn_readlane(len_reg, sq) : clamped_len(a, sq);
     };
@@ -770,20 +785,32 @@ void decode_mfma_kernel(const DecodeArgs a) {
             }
         }
         if (nch == 0) return;
-        int g = static_cast<int>((start - seq_base) / nch);
-        int c0 = static_cast<int>((start - seq_base) % nch);
+        // g: the pair (with head groups, the group) of the first segment;
+        // c0, c1: the segment's first and end entries in that pair's (group's)
+        // part of the list, which holds span entries.
+        int HG = seq_hg(nch) ? 4 : 1;             // pairs one segment of this sequence covers
+        int64_t span = static_cast<int64_t>(HG) * nch;
+        int g = static_cast<int>((start - seq_base) / span);
+        int c0 = static_cast<int>((start - seq_base) % span);
         int64_t pos = start;
 
         for (;;) {
-            const int c1 = static_cast<int>(nch - c0 < end - pos ? nch : c0 + (end - pos));
+            const int c1 = static_cast<int>(span - c0 < end - pos ? span : c0 + (end - pos));
             const int n_seg = c1 - c0;
             const int n_local = n_seg > wave ? (n_seg - wave + kWaves - 1) / kWaves : 0;
+            // This wave's entries are c0 + wave + 4k (k < n_local): chunks
+            // cb + cs*k of (virtual) KV head gw.
+            const bool hgs = HG == 4;
+            const int jw = hgs ? (c0 + wave) & 3 : 0;
+            const int gw = hgs ? HG * g + jw : g;
+            const int cb = hgs ? (c0 + wave) >> 2 : c0 + wave;
+            const int cs = hgs ? 1 : kWaves;
             const int c_rag = (L % kChunk) ? nch - 1 : -1;
             const uint32_t rag_bytes = static_cast<uint32_t>(L - ((nch - 1) * kChunk / BS) * BS) * row_bytes;
-            const int h0 = g * G;
+            const int h0 = gw * G;
             const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
             const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
-            const size_t head_off = static_cast<size_t>(g / a.kv_split) * D * 2 * (a.head_major ? BS : 1);
+            const size_t head_off = static_cast<size_t>(gw / a.kv_split) * D * 2 * (a.head_major ? BS : 1);
             const char* kbase = reinterpret_cast<const char*>(a.k_cache) + head_off;
             const char* vbase = reinterpret_cast<const char*>(a.v_cache) + head_off;
 
@@ -810,7 +837,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
             for (int kw = 0; kw < n_local; kw += kWave) {
                 int ids = -1;
                 {
-                    const int c = c0 + wave + (kw + lane) * kWaves;
+                    const int c = cb + (kw + lane) * cs;
                     if (kw + lane < n_local) {
                         const int id = trow[c * kChunk / BS];
                         ids = (id < 0 || id >= a.num_blocks) ? -1 : id;
@@ -825,7 +852,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
                     int rem;                // tokens of the context from the chunk's first on
                 };
                 auto source = [&](int k, bool live) -> Src {
-                    const int c = c0 + wave + (kw + k) * kWaves;
+                    const int c = cb + (kw + k) * cs;
                     int blk = __builtin_amdgcn_readlane(ids, k & (kWave - 1));
                     const bool blk_ok = blk >= 0;
                     blk = blk_ok ? blk : 0;
@@ -871,7 +898,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
                     }
                     const Src nxt = source(k2, live2);
                     issue_k(kd, nxt);
-                    const bool need_mask = !cur.blk_ok || (c0 + wave + (kw + k) * kWaves) == c_rag;
+                    const bool need_mask = !cur.blk_ok || (cb + (kw + k) * cs) == c_rag;
                     const bool tok_ok = cur.blk_ok && t_lane < cur.rem;
                     const bool b3 = lp & 2, b2 = lp & 1;
                     float pr[RS];
@@ -993,60 +1020,98 @@ void decode_mfma_kernel(const DecodeArgs a) {
                 }
             }
 
-            // Row sums over the chunk tokens of this wave; then to LDS.
+            if (hgs) {
+                // Each wave finishes its own pair (sequence s, head gw): the
+                // running max and the row sum of head 4r + i sit in lane 4i.
+                if (n_local > 0) {
+                    const bool whole = c0 <= jw && c1 > 4 * (nch - 1) + jw;
+                    const size_t slot = 4 * (static_cast<size_t>(unit) + static_cast<size_t>(s) * (Hkv / 4) + g) + jw;
 #pragma unroll
-            for (int r = 0; r < RS; ++r) {
-                const float lw = tok_sum(l_run[r]);
-                const int h = 4 * r + lp;
-                if (ltg == 0 && lj == 0 && h < G) {
-                    s_m[wave][h] = m_run[r];
-                    s_l[wave][h] = lw;
+                    for (int r = 0; r < RS; ++r) {
+                        const float lw = tok_sum(l_run[r]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int h = 4 * r + i;
+                            if (h >= G) continue;
+                            const float mh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_run[r]), 4 * i));
+                            const float lh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lw), 4 * i));
+#pragma unroll
+                            for (int n = 0; n < NG; ++n) {
+                                const int d = 64 * n + lane;
+                                const float num = acc[r][n][i];
+                                if (whole) {
+                                    const float o = lh == 0.f ? 0.f : num / lh;
+                                    a.out[out_row0 + h * D + d] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(o));
+                                } else {
+                                    a.part_o[(slot * G + h) * D + d] = num;
+                                }
+                            }
+                            if (!whole && lane == 0) {
+                                a.part_ml[(slot * G + h) * 2] = mh;
+                                a.part_ml[(slot * G + h) * 2 + 1] = lh;
+                            }
+                        }
+                    }
                 }
+            } else {
+                // Row sums over the chunk tokens of this wave; then to LDS.
 #pragma unroll
-                for (int n = 0; n < NG; ++n)
+                for (int r = 0; r < RS; ++r) {
+                    const float lw = tok_sum(l_run[r]);
+                    const int h = 4 * r + lp;
+                    if (ltg == 0 && lj == 0 && h < G) {
+                        s_m[wave][h] = m_run[r];
+                        s_l[wave][h] = lw;
+                    }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (4 * r + i < G) s_acc[wave][4 * r + i][64 * n + lane] = acc[r][n][i];
-            }
-            __syncthreads();
+                    for (int n = 0; n < NG; ++n)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (4 * r + i < G) s_acc[wave][4 * r + i][64 * n + lane] = acc[r][n][i];
+                }
+                __syncthreads();
 
-            const bool whole = c0 == 0 && c1 == nch;
-            const size_t slot = static_cast<size_t>(unit) + static_cast<size_t>(s) * Hkv + g;
-            for (int o = threadIdx.x; o < G * D; o += kThreads) {
-                const int h = o / D;
-                const int d = o % D;
-                float mm = s_m[0][h];
+                const bool whole = c0 == 0 && c1 == nch;
+                const size_t slot = hg_mode ? 4 * (static_cast<size_t>(unit) + static_cast<size_t>(s) * (Hkv / 4) + (g >> 2)) + (g & 3)
+                                            : static_cast<size_t>(unit) + static_cast<size_t>(s) * Hkv + g;
+                for (int o = threadIdx.x; o < G * D; o += kThreads) {
+                    const int h = o / D;
+                    const int d = o % D;
+                    float mm = s_m[0][h];
 #pragma unroll
-                for (int v = 1; v < kWaves; ++v) mm = __builtin_fmaxf(mm, s_m[v][h]);
-                float num = 0.f, den = 0.f;
+                    for (int v = 1; v < kWaves; ++v) mm = __builtin_fmaxf(mm, s_m[v][h]);
+                    float num = 0.f, den = 0.f;
 #pragma unroll
-                for (int v = 0; v < kWaves; ++v) {
-                    const float f = fast_exp2(s_m[v][h] - mm);
-                    num = __builtin_fmaf(f, s_acc[v][h][d], num);
-                    den = __builtin_fmaf(f, s_l[v][h], den);
-                }
-                if (whole) {
-                    const float r = den == 0.f ? 0.f : num / den;
-                    a.out[out_row0 + o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
-                } else {
-                    a.part_o[(slot * G + h) * D + d] = num;
-                    if (d == 0) {
-                        a.part_ml[(slot * G + h) * 2] = mm;
-                        a.part_ml[(slot * G + h) * 2 + 1] = den;
+                    for (int v = 0; v < kWaves; ++v) {
+                        const float f = fast_exp2(s_m[v][h] - mm);
+                        num = __builtin_fmaf(f, s_acc[v][h][d], num);
+                        den = __builtin_fmaf(f, s_l[v][h], den);
+                    }
+                    if (whole) {
+                        const float r = den == 0.f ? 0.f : num / den;
+                        a.out[out_row0 + o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
+                    } else {
+                        a.part_o[(slot * G + h) * D + d] = num;
+                        if (d == 0) {
+                            a.part_ml[(slot * G + h) * 2] = mm;
+                            a.part_ml[(slot * G + h) * 2 + 1] = den;
+                        }
                     }
                 }
             }
 
             pos += n_seg;
             if (pos >= end) break;
-            __syncthreads();
+            if (!hgs) __syncthreads();               // LDS is reused by the next segment
             c0 = 0;
-            if (++g == Hkv) {
+            if (++g == Hkv / HG) {
                 g = 0;
                 L = 0;
                 while (L == 0 && s + 1 < a.num_seqs) L = len_of(++s);
                 nch = chunks_of(L);
                 if (nch == 0) break;
+                HG = seq_hg(nch) ? 4 : 1;
+                span = static_cast<int64_t>(HG) * nch;
             }
         }
     };
@@ -1076,7 +1141,8 @@ void decode_mfma_kernel(const DecodeArgs a) {
 // rows of empty contexts.  One workgroup of 4 waves per (sequence, KV head)
 // pair; pairs the split kernel wrote whole return at once.
 //
-// A pair's partial output of split v is G*D contiguous floats (slot v + pair).
+// A pair's partial output of split v is G*D contiguous floats (slot v + pair,
+// or 4 * (v + group) + head in group when the split kernel ran head groups).
 // The threads form kS groups of kT = G*D/4 threads: thread (grp, t) takes the
 // 16-byte piece t of splits w0 + grp, w0 + grp + kS, ..., with each split's
 // (max, sum) for the piece's head, and folds them in split order into its own
@@ -1118,14 +1184,27 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
         before += wave_sum64(sl < s ? n : 0);
     }
     const int64_t U = uniform64(total) * Hkv;
-    const int64_t first = uniform64(before) * Hkv + static_cast<int64_t>(g) * nch;
+    // The pair's entries in the list: first, first + step, ... (nch of them);
+    // in the head-group order (decided as in the split kernel, per sequence)
+    // a group's 4 heads interleave chunk by chunk.
+    const bool hg_mode = a.head_groups && U >= 4 * static_cast<int64_t>(N);
+    const bool hgs = hg_mode && 4 * static_cast<int64_t>(nch) * N <= 30 * U;
+    const int64_t step = hgs ? 4 : 1;
+    const int64_t first = uniform64(before) * Hkv +
+                          (hgs ? static_cast<int64_t>(g & ~3) * nch + (g & 3) : static_cast<int64_t>(g) * nch);
     const int w0 = owner_of(first, U, N);
-    const int w1 = owner_of(first + nch - 1, U, N);
+    const int w1 = owner_of(first + step * (nch - 1), U, N);
     if (w0 == w1) return;                         // written whole by the split kernel
     const int P = w1 - w0 + 1;
     const bool may_be_empty = U < N;              // some splits then hold no chunk
     auto empty_split = [&](int64_t v) { return v * U / N == (v + 1) * U / N; };
     const size_t pair = static_cast<size_t>(s) * Hkv + g;
+    // Partial slot of split v: v + pair, or, with head groups allowed (in
+    // either order), 4 * (v + group) + head in group.
+    auto slot_of = [&](int64_t v) -> size_t {
+        return hg_mode ? 4 * (static_cast<size_t>(v) + static_cast<size_t>(s) * (Hkv / 4) + (g >> 2)) + (g & 3)
+                       : static_cast<size_t>(v) + pair;
+    };
 
     __shared__ float s_m[kS][kT], s_l[kS][kT];
     __shared__ float4 s_o[kS][kT];
@@ -1148,7 +1227,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
                 po[k] = make_float4(0.f, 0.f, 0.f, 0.f);
                 pml[k] = make_float2(-__builtin_inff(), 0.f);
                 if (live) {
-                    const size_t slot = static_cast<size_t>(v) + pair;
+                    const size_t slot = slot_of(v);
                     po[k] = *reinterpret_cast<const float4*>(a.part_o + slot * kO + 4 * t);
                     pml[k] = *reinterpret_cast<const float2*>(a.part_ml + (slot * G + h) * 2);
                 }
@@ -1315,6 +1394,10 @@ GroupSplit decode_group_split(int group) {
     int g = 8;
     while (group % g != 0) --g;
     return {g, group / g};
+}
+
+bool decode_head_groups_ok(int block_size, int group, int virtual_kv_heads) {
+    return block_size >= kChunk && group >= 3 && group <= 8 && virtual_kv_heads % 4 == 0;
 }
 
 bool decode_supported(int head_dim, int block_size, int group) {

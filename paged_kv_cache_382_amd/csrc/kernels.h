@@ -33,6 +33,10 @@ struct DecodeArgs {
     int32_t head_major;            // 1: cache [NB][Hkv][BS][D], else [NB][BS][Hkv][D]
     int32_t kv_split;              // virtual KV heads per KV head (>= 1): a query group of
                                    // G > 8 heads runs as kv_split groups of G / kv_split
+    int32_t head_groups;           // 1: the matrix-core kernel may order each sequence's chunk
+                                   // list by groups of 4 (virtual) KV heads (decode.hip); needs
+                                   // num_kv_heads * kv_split % 4 == 0 and 4 * N + pairs slots;
+                                   // the host sets it for the slot-major layout only
 };
 
 // The query group a decode kernel takes (at most 8 heads) and how many such
@@ -45,6 +49,10 @@ GroupSplit decode_group_split(int group);
 
 // group: heads per kernel group (1..8, after decode_group_split).
 bool decode_supported(int head_dim, int block_size, int group);
+// Whether the kernel for this block size and group (1..8) can order the chunk
+// list by head groups: the matrix-core kernel, with a multiple of 4 (virtual)
+// KV heads.
+bool decode_head_groups_ok(int block_size, int group, int virtual_kv_heads);
 // Workgroups of the decode kernel for these shapes that the current device
 // holds at once; 0 when no device can be queried.
 int decode_resident_workgroups(int head_dim, int block_size, int group);

@@ -174,11 +174,19 @@ def test_copy_blocks_rejects_bad_arguments():
 def test_workspace_and_split_queries():
     d = _desc(nb=8192, bs=16, hkv=8, d=128)
     assert pa.pa_decode_num_splits(d, 32, 512) == 512
-    # (512 splits + 4 sequences x 8 KV heads) slots x 4 heads x (2 + 128) floats
-    assert pa.pa_decode_workspace_bytes(d, 4, 32, 512) == (512 + 32) * 4 * (2 + 128) * 4
+    # head-group order (4 query heads a KV head on the matrix cores, 8 KV heads):
+    # (4 x 512 splits + 4 sequences x 8 KV heads) slots x 4 heads x (2 + 128) floats
+    assert pa.pa_decode_workspace_bytes(d, 4, 32, 512) == (4 * 512 + 32) * 4 * (2 + 128) * 4
     n = pa.pa_decode_num_splits(d, 32, 0)
     assert n > 0
-    assert pa.pa_decode_workspace_bytes(d, 4, 32, 0) == (n + 32) * 4 * (2 + 128) * 4
+    assert pa.pa_decode_workspace_bytes(d, 4, 32, 0) == (4 * n + 32) * 4 * (2 + 128) * 4
+    # plain order: 2 KV heads (not a multiple of 4), or one query head a KV head
+    d2 = _desc(nb=8192, bs=16, hkv=2, d=128)
+    assert pa.pa_decode_workspace_bytes(d2, 4, 8, 512) == (512 + 8) * 4 * (2 + 128) * 4
+    assert pa.pa_decode_workspace_bytes(d, 4, 8, 512) == 512 * 1 * (2 + 128) * 4 + 32 * 1 * (2 + 128) * 4
+    # blocks of 8 tokens run on the vector kernel: plain order
+    d3 = _desc(nb=8192, bs=8, hkv=8, d=128)
+    assert pa.pa_decode_workspace_bytes(d3, 4, 32, 512) == (512 + 32) * 4 * (2 + 128) * 4
     assert pa.pa_decode_workspace_bytes(d, 4, 33, 0) == 0             # invalid -> 0
     assert pa.pa_decode_num_splits(d, 32, -3) == 0
 

@@ -261,23 +261,60 @@ def test_decode_full_size(name, seqs, n_split):
     check_close(out if seqs is None else out[seqs], ref, name)
 
 
+@pytest.mark.parametrize("N", [64, 200])
+def test_decode_head_group_and_plain_orders_in_one_call(N):
+    """Slot-major, 4 query heads per KV head, 4 KV heads: a sequence takes the
+    head-group order while its groups span at most about 32 splits
+    (4 * chunks * N <= 30 * U; here U = 4 * 341 chunks).  At N = 64 the
+    4 000-token sequence (250 chunks) runs the plain order and the others the
+    head-group order; at N = 200 the 1 000-token one (63 chunks) also runs the
+    plain order.  Every row against the oracle; the same call with the plain
+    order's workspace (every sequence plain) too."""
+    lens = [4000, 100, 300, 17, 1000]
+    wl = W.shrink(MEDIUM, name="orders", num_seqs=len(lens))
+    p = build(wl, plan_fn=medium_plan(wl, lens))
+    out = run_step(p, num_splits=N)
+    kc, vc = oracle_caches(p)
+    ref = oracle_out(p, kc, vc)
+    check_close(out, ref, f"mixed orders N={N}")
+    B = p["q"].shape[0]
+    desc_h = pa.cache_desc(p["kc"])                  # same sizes, head-major: plain order only
+    desc_h.layout = pa.LAYOUTS["head"]
+    plain = pa.decode_workspace(desc_h, B, wl.num_q_heads, N, DEV)
+    assert plain.numel() < pa.pa_decode_workspace_bytes(pa.cache_desc(p["kc"]), B, wl.num_q_heads, N)
+    say(f"orders: plain-order workspace, N={N}")
+    out_p = pa.pa_decode(p["q"], p["kc"], p["vc"], p["tables"], p["lens"], wl.scale,
+                         max_context_len=p["max_ctx"], num_splits=N, workspace=plain)
+    torch.cuda.synchronize()
+    check_close(out_p, ref, f"plain order N={N}")
+
+
 def test_decode_full_size_mix_head_major():
     """The mixed-length workload with the head-major cache: bitwise equal to
-    the slot-major call (same arithmetic, other addresses) and within the bar
-    of the oracle for every sequence."""
+    the slot-major call in the same (plain) order, which slot-major runs when
+    given the plain order's workspace (same arithmetic, other addresses); the
+    head-major result and the slot-major result in its default head-group
+    order both within the bar of the oracle for every sequence."""
     wl = W.MIX
     p = build(wl, fill="random")
-    out_s = run_step(p)
+    out_sd = run_step(p)                       # default workspace: head-group order
     nb, bs, hkv, d = p["kc"].shape
     kh = p["kc"].transpose(1, 2).contiguous()
     vh = p["vc"].transpose(1, 2).contiguous()
+    B = p["q"].shape[0]
+    plain = pa.decode_workspace(pa.cache_desc(kh, "head"), B, wl.num_q_heads, 0, DEV)
+    say("mix slot-major, plain order: pa_decode")
+    out_s = pa.pa_decode(p["q"], p["kc"], p["vc"], p["tables"], p["lens"], wl.scale,
+                         max_context_len=p["max_ctx"], workspace=plain)
     say("mix head-major: pa_decode")
     out_h = pa.pa_decode(p["q"], kh, vh, p["tables"], p["lens"], wl.scale,
                          max_context_len=p["max_ctx"], layout="head")
     torch.cuda.synchronize()
     assert torch.equal(out_h.view(torch.int16), out_s.view(torch.int16))
     kc, vc = oracle_caches(p)
-    check_close(out_h, oracle_out(p, kc, vc), "mix head-major")
+    ref = oracle_out(p, kc, vc)
+    check_close(out_h, ref, "mix head-major")
+    check_close(out_sd, ref, "mix slot-major, head-group order")
 
 
 GROUPS = [(g, bs, d) for g, bs, d in [(3, 16, 128), (3, 8, 64), (5, 16, 64), (5, 8, 128), (6, 32, 128),

@@ -2,7 +2,10 @@
 
 The layout only moves rows inside a block, and every kernel does the same
 arithmetic in the same order either way, so decode and prefill over a
-head-major copy of a cache must equal the slot-major results bit for bit; the
+head-major copy of a cache must equal the slot-major results bit for bit (for
+decode in the same order: given the plain order's workspace, slot-major runs
+the plain order that head-major runs; with its own, larger workspace it may
+run the head-group order, which is checked against the oracle); the
 store must put every head's piece where the oracle's head-major store does; and
 the outputs must be within the parity bar of the oracle run on the head-major
 arrays themselves.
@@ -92,8 +95,12 @@ def test_head_major_decode_equals_slot_major_and_oracle(case, num_splits):
     ll = torch.tensor(lens, dtype=torch.int32, device=DEV)
     scale = float(np.float32(1.0 / np.sqrt(d)))
     say(f"decode layouts bs {bs} hkv {hkv} d {d} g {g} splits {num_splits}")
-    out_s = pa.pa_decode(q, kc, vc, t, ll, scale, max_context_len=max(lens), num_splits=num_splits)
     kh, vh = head_major(kc), head_major(vc)
+    # the plain order's workspace (head-major never takes the head-group order)
+    plain = pa.decode_workspace(pa.cache_desc(kh, "head"), len(lens), hkv * g, num_splits, DEV)
+    out_s = pa.pa_decode(q, kc, vc, t, ll, scale, max_context_len=max(lens), num_splits=num_splits,
+                         workspace=plain)
+    out_sd = pa.pa_decode(q, kc, vc, t, ll, scale, max_context_len=max(lens), num_splits=num_splits)
     out_h = pa.pa_decode(q, kh, vh, t, ll, scale, max_context_len=max(lens), num_splits=num_splits,
                          layout="head")
     torch.cuda.synchronize()
@@ -101,6 +108,7 @@ def test_head_major_decode_equals_slot_major_and_oracle(case, num_splits):
     ref = decode_ref(host_u16(q).view(np.float16), host_u16(kh).view(np.float16),
                      host_u16(vh).view(np.float16), tables, lens, scale, layout="head")
     check_close(out_h, ref, "head-major decode")
+    check_close(out_sd, ref, "slot-major decode, default workspace")
 
 
 @pytest.mark.parametrize("g,bs,d", [(1, 16, 128), (4, 16, 128), (2, 8, 128), (8, 32, 64), (3, 64, 64)])
