@@ -38,8 +38,10 @@
 //  * A segment that covers a whole pair is normalised and written to fp16
 //    directly.  Otherwise the workgroup writes fp32 (m, l, o) partials to
 //    slot w + pair of the workspace (distinct for every segment: along the
-//    chunk order, either w or pair grows at each segment start), and the merge
-//    kernel combines the slots of workgroups first(pair) .. last(pair).
+//    chunk order, either w or pair grows at each segment start; in the
+//    matrix-core kernel's head-group order, slot 4 * (w + group) + head in
+//    group), and the merge kernel combines the slots of workgroups
+//    first(pair) .. last(pair).
 //  * Within a segment, chunks are dealt round-robin to the 4 wave64s of the
 //    workgroup.  A K (or V) row of D fp16 is D/8 lanes x 16 bytes, so one
 //    buffer_load_dwordx4 per lane covers 64/(D/8) whole rows (1 KiB per wave
@@ -604,8 +606,11 @@ void decode_split_kernel(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Matrix-core variant for 3 to 8 query heads per KV head (block size >= 16).
 //
-// Same partition, workspace and merge as decode_split_kernel; only the work
-// on a segment differs.  The G query rows of a KV head are the rows of
+// Same partition, workspace and merge as decode_split_kernel, except that on
+// the slot-major layout with a multiple of 4 KV heads a sequence's part of the
+// chunk list may run in the head-group order (groups of 4 heads, chunk-major
+// inside a group, one head per wave; see hg_mode below), whose partial slots
+// are 4 * (split + group) + head in group.  The work on a segment:  The G query rows of a KV head are the rows of
 // v_mfma_f32_4x4x4_16b_f16 tiles (one set of 4 rows for G <= 4, two for
 // G <= 8; rows past G hold zero queries and are never written), so that the
 // products run on the matrix cores and the vector ALUs only keep the
