@@ -281,6 +281,16 @@ pa_status decode_call(const char* fn, const void* q, const void* k_cache, const 
         a.head_major = cache->layout == PA_LAYOUT_HEAD_MAJOR;
         a.kv_split = gsplit.kv_split;
         a.head_groups = hg ? 1 : 0;
+        // With the split count left to the library, a batch whose sequences all
+        // take the head-group order runs on two workgroups a compute unit (the
+        // kernels decide, from the lengths they read): it streams faster so
+        // (mixed lengths 101.6 vs 104.3 us a call, prefix sharing 66.5 vs 77.6),
+        // while the plain order keeps three (4 x 131072 tokens 341 vs 355 us).
+        a.num_splits_hg = 0;
+        if (hg && num_splits == 0) {
+            const int cus = decode_compute_units();
+            if (cus > 0 && splits > 2 * cus) a.num_splits_hg = 2 * cus;
+        }
         a.whole_pairs = 0;
         if (num_splits == kWholePairs && num_seqs > 64)
             return fail(PA_ERR_RANGE, "%s: num_splits -1 (whole pairs) takes at most 64 sequences", fn);

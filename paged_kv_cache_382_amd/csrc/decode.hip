@@ -174,6 +174,30 @@ __device__ __forceinline__ int owner_of(int64_t x, int64_t U, int W) {
     return static_cast<int>(((x + 1) * W - 1) / U);
 }
 
+// Most chunks of any one sequence (wave-uniform result).
+__device__ int max_chunks(const DecodeArgs& a, int lane) {
+    int m = 0;
+    for (int b0 = 0; b0 < a.num_seqs; b0 += kWave) {
+        const int s = b0 + lane;
+        int x = s < a.num_seqs ? chunks_of(clamped_len(a, s)) : 0;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) x = max(x, __shfl_xor(x, o, kWave));
+        m = max(m, x);
+    }
+    return uniform(m);
+}
+
+// The split count the matrix-core and merge kernels work with: num_splits,
+// or the smaller num_splits_hg (two workgroups a compute unit, which the
+// head-group order streams faster with) when every sequence would take the
+// head-group order with it.  Workgroups past it have no work.  U: chunks of
+// the list.
+__device__ int splits_in_use(const DecodeArgs& a, int64_t U, int lane) {
+    const int N = a.num_splits, Nh = a.num_splits_hg;
+    if (!a.head_groups || a.whole_pairs || Nh <= 0 || Nh >= N || U < 4 * static_cast<int64_t>(Nh)) return N;
+    return 4 * static_cast<int64_t>(max_chunks(a, lane)) * Nh <= 30 * U ? Nh : N;
+}
+
 template <int D>
 struct Geometry {
     static constexpr int LPR = D / 8;            // lanes per token row
@@ -717,7 +741,6 @@ void decode_mfma_kernel(const DecodeArgs a) {
     // (sequence, KV head) pairs per sequence: virtual heads when a large
     // query group is cut into several (each re-reads its KV head's rows).
     const int Hkv = a.num_kv_heads * a.kv_split;
-    const int N = a.num_splits;
 
     const uint32_t row_bytes = a.head_major ? D * 2 : static_cast<uint32_t>(a.num_kv_heads) * D * 2;
     const uint32_t block_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2 * BS;
@@ -739,6 +762,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int len_reg = (lens_in_regs && lane < a.num_seqs) ? clamped_len(a, lane) : 0;
     const int64_t incl_reg = wave_incl_scan64(chunks_of(len_reg), lane);
     const int64_t U = (lens_in_regs ? readlane64(incl_reg, kWave - 1) : chunks_per_head(a, lane)) * Hkv;
+    const int N = splits_in_use(a, U, lane);
     // Head groups: a sequence's part of the list may run group by group of 4
     // (virtual) KV heads, chunk-major inside a group with the group's heads
     // interleaved (entry 4c + j: chunk c of head 4*hg + j).  Each wave then
@@ -1136,6 +1160,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
         start = (readlane64(incl_reg, s) - nch) * Hkv + static_cast<int64_t>(g) * nch;
         end = start + nch;
     } else {
+        if (u >= N) return;                       // beyond the split count in use
         start = static_cast<int64_t>(u) * U / N;
         end = static_cast<int64_t>(u + 1) * U / N;
     }
@@ -1170,7 +1195,6 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
     // (sequence, KV head) pairs per sequence: virtual heads when a large
     // query group is cut into several (each re-reads its KV head's rows).
     const int Hkv = a.num_kv_heads * a.kv_split;
-    const int N = a.num_splits;
     const int s = blockIdx.x / Hkv;
     const int g = blockIdx.x % Hkv;
     const int L = uniform(clamped_len(a, s));
@@ -1189,6 +1213,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
         before += wave_sum64(sl < s ? n : 0);
     }
     const int64_t U = uniform64(total) * Hkv;
+    const int N = splits_in_use(a, U, lane);
     // The pair's entries in the list: first, first + step, ... (nch of them);
     // in the head-group order (decided as in the split kernel, per sequence)
     // a group's 4 heads interleave chunk by chunk.
@@ -1329,9 +1354,9 @@ int resident_one() {
         (void)hipGetLastError();
         return 0;
     }
-    // The matrix-core kernel fits 4 workgroups a CU, but 3 stream faster
-    // (measured: 4 x 131072-token contexts 342 vs 370 us a call, mixed lengths
-    // 104 vs 105 us); the vector kernels use what fits.
+    // The matrix-core kernel runs 3 workgroups a CU (its register budget;
+    // 4 had streamed slower: 4 x 131072-token contexts 342 vs 370 us a call);
+    // the vector kernels use what fits.
     if (use_mfma<BS, G>() && per_cu > 3) per_cu = 3;
     v = per_cu * cus;
     if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
@@ -1410,6 +1435,21 @@ bool decode_supported(int head_dim, int block_size, int group) {
     const bool b_ok = block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
     const bool g_ok = group >= 1 && group <= 8;      // larger groups are cut into these
     return d_ok && b_ok && g_ok;
+}
+
+int decode_compute_units() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 int decode_resident_workgroups(int head_dim, int block_size, int group) {

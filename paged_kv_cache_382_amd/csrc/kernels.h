@@ -37,6 +37,9 @@ struct DecodeArgs {
                                    // list by groups of 4 (virtual) KV heads (decode.hip); needs
                                    // num_kv_heads * kv_split % 4 == 0 and 4 * N + pairs slots;
                                    // the host sets it for the slot-major layout only
+    int32_t num_splits_hg;         // 0, or a split count below num_splits (two workgroups a
+                                   // compute unit) that the matrix-core and merge kernels use
+                                   // instead when every sequence then takes the head-group order
 };
 
 // The query group a decode kernel takes (at most 8 heads) and how many such
@@ -56,6 +59,8 @@ bool decode_head_groups_ok(int block_size, int group, int virtual_kv_heads);
 // Workgroups of the decode kernel for these shapes that the current device
 // holds at once; 0 when no device can be queried.
 int decode_resident_workgroups(int head_dim, int block_size, int group);
+// Compute units of the current device; 0 when it cannot be queried.
+int decode_compute_units();
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Arguments of one chunked-prefill call, already checked by the caller.
