@@ -1355,9 +1355,13 @@ int resident_one() {
         return 0;
     }
     // The matrix-core kernel runs 3 workgroups a CU (its register budget;
-    // 4 had streamed slower: 4 x 131072-token contexts 342 vs 370 us a call);
-    // the vector kernels use what fits.
+    // 4 had streamed slower: 4 x 131072-token contexts 342 vs 370 us a call).
+    // The vector kernel for 1 or 2 query heads a KV head fits 4 but streams
+    // faster on 2 (32 x 2048 tokens, 32/32 heads: 171 vs 178.5 us a call;
+    // mixed lengths 362 vs 366); for 4 or more (blocks of 8) it keeps what fits
+    // (4 x 131072 tokens at block 8: 3 a CU, 362 vs 380 us on 2).
     if (use_mfma<BS, G>() && per_cu > 3) per_cu = 3;
+    if (!use_mfma<BS, G>() && G <= 2 && per_cu > 2) per_cu = 2;
     v = per_cu * cus;
     if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
     return v;
