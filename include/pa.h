@@ -197,8 +197,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* cach
  *
  * Supported: head_dim 64 or 128; block_size 8, 16, 32 or 64; num_q_heads any
  * multiple of num_kv_heads.  A group G = num_q_heads / num_kv_heads of up to 8
- * query heads shares each K/V read (groups of 3 to 8 on matrix cores when
- * block_size >= 16); a larger group runs as G / g groups of its largest
+ * query heads shares each K/V read (groups of 3 to 8 on matrix cores); a
+ * larger group runs as G / g groups of its largest
  * divisor g <= 8, each reading its KV head's rows again (the workspace and
  * the split count then cover num_kv_heads * G / g pairs per sequence).  Other
  * shapes return PA_ERR_UNSUPPORTED.  Results depend only on the context lengths,

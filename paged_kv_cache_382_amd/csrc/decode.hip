@@ -20,9 +20,9 @@
 // with K/V row p found in physical block table[s][p / BS], row p % BS.
 //
 // Design (HBM-bound streaming).  This vector kernel (decode_split_kernel)
-// serves 1 or 2 query heads per KV head and block size 8; 3 to 8 query heads
-// per KV head run the same partition on the matrix cores (decode_mfma_kernel,
-// below), and larger groups are cut into virtual KV heads of at most 8:
+// serves 1 or 2 query heads per KV head; 3 to 8 query heads per KV head run
+// the same partition on the matrix cores (decode_mfma_kernel, below), and
+// larger groups are cut into virtual KV heads of at most 8:
 //  * Short contexts (a bound of at most 512 tokens, at most 64 sequences):
 //    workgroup w takes (sequence, KV head) pair w whole and writes its fp16
 //    rows; no merge kernel runs.  One launch instead of two where launch
@@ -716,7 +716,8 @@ constexpr int mfma_waves_per_simd() { return G <= 4 ? 3 : 2; }
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<G>())))
 void decode_mfma_kernel(const DecodeArgs a) {
-    static_assert(BS >= kChunk, "one block per chunk");
+    static_assert(BS >= kChunk || 2 * BS == kChunk, "one or two blocks per chunk");
+    constexpr int BPC = BS >= kChunk ? 1 : 2;     // blocks per chunk
     constexpr int RS = mfma_row_sets<G>();        // sets of 4 query rows
     constexpr int KM = D / 32;                    // K loads per chunk (4 or 8 whole rows each)
     constexpr int SL = D / 8;                     // 16-byte slices of a row
@@ -836,6 +837,11 @@ void decode_mfma_kernel(const DecodeArgs a) {
             const int cs = hgs ? 1 : kWaves;
             const int c_rag = (L % kChunk) ? nch - 1 : -1;
             const uint32_t rag_bytes = static_cast<uint32_t>(L - ((nch - 1) * kChunk / BS) * BS) * row_bytes;
+            // Two blocks a chunk: the ragged chunk's rows in its first and
+            // second block (rag_bytes counts them from the first).
+            const int rag_rows = L - (nch - 1) * kChunk;
+            const uint32_t rag_lo = static_cast<uint32_t>(rag_rows < BS ? rag_rows : BS) * row_bytes;
+            const uint32_t rag_hi = static_cast<uint32_t>(rag_rows > BS ? rag_rows - BS : 0) * row_bytes;
             const int h0 = gw * G;
             const size_t out_row0 = (static_cast<size_t>(s) * a.num_q_heads + h0) * D;
             const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
@@ -864,20 +870,26 @@ void decode_mfma_kernel(const DecodeArgs a) {
             }
 
             for (int kw = 0; kw < n_local; kw += kWave) {
-                int ids = -1;
+                int ids = -1, ids2 = -1;               // ids2: a chunk's second block
                 {
                     const int c = cb + (kw + lane) * cs;
                     if (kw + lane < n_local) {
                         const int id = trow[c * kChunk / BS];
                         ids = (id < 0 || id >= a.num_blocks) ? -1 : id;
+                        // The second block's entry exists only if it holds tokens.
+                        if (BPC == 2 && c * kChunk + BS < L) {
+                            const int id2 = trow[c * kChunk / BS + 1];
+                            ids2 = (id2 < 0 || id2 >= a.num_blocks) ? -1 : id2;
+                        }
                     }
                 }
                 const int nw = n_local - kw < kWave ? n_local - kw : kWave;
 
                 struct Src {
-                    __amdgpu_buffer_rsrc_t kr, vr;
+                    __amdgpu_buffer_rsrc_t kr, vr;   // the chunk's (first) block
+                    __amdgpu_buffer_rsrc_t kr2, vr2; // two blocks a chunk: tokens BS .. 2BS-1
                     int soff;               // byte offset of the chunk's first row in its block
-                    bool blk_ok;
+                    bool ok_lo, ok_hi;      // table entries of tokens 0 .. BS-1 and BS .. in range
                     int rem;                // tokens of the context from the chunk's first on
                 };
                 auto source = [&](int k, bool live) -> Src {
@@ -885,14 +897,30 @@ void decode_mfma_kernel(const DecodeArgs a) {
                     int blk = __builtin_amdgcn_readlane(ids, k & (kWave - 1));
                     const bool blk_ok = blk >= 0;
                     blk = blk_ok ? blk : 0;
-                    const uint32_t full = c == c_rag ? rag_bytes : block_bytes;
+                    const bool rag = c == c_rag;
+                    const uint32_t full = rag ? (BPC == 2 ? rag_lo : rag_bytes) : block_bytes;
                     const uint32_t range = (live && blk_ok) ? full : 0u;
                     const size_t boff = static_cast<size_t>(blk) * block_bytes;
                     Src r;
                     r.kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + boff), 0, range, kRsrcWord3);
                     r.vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + boff), 0, range, kRsrcWord3);
+                    r.kr2 = r.kr;
+                    r.vr2 = r.vr;
+                    r.ok_lo = r.ok_hi = blk_ok;
+                    if constexpr (BPC == 2) {
+                        // A block id of -1 here is an entry out of range or a
+                        // block holding no token of the context; either way its
+                        // rows read as zeros and their scores are masked.
+                        int blk2 = __builtin_amdgcn_readlane(ids2, k & (kWave - 1));
+                        const bool ok2 = blk2 >= 0;
+                        blk2 = ok2 ? blk2 : 0;
+                        const uint32_t range2 = (live && ok2) ? (rag ? rag_hi : block_bytes) : 0u;
+                        const size_t boff2 = static_cast<size_t>(blk2) * block_bytes;
+                        r.kr2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + boff2), 0, range2, kRsrcWord3);
+                        r.vr2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + boff2), 0, range2, kRsrcWord3);
+                        r.ok_hi = ok2;
+                    }
                     r.soff = static_cast<int>((static_cast<uint32_t>(c * kChunk) % BS) * row_bytes);
-                    r.blk_ok = blk_ok;
                     r.rem = L - c * kChunk;
                     return r;
                 };
@@ -901,13 +929,24 @@ void decode_mfma_kernel(const DecodeArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                     return r;
                 };
+                // Load m (v) holds rows TPL*m (RPL*v) on: with two blocks a
+                // chunk, the first half of the loads reads the first block and
+                // the second half the second, each from its block's row 0.
                 auto issue_k = [&](uint4 (&kd)[KM], const Src& r) {
 #pragma unroll
-                    for (int m = 0; m < KM; ++m) kd[m] = load(r.kr, k_lane_off, r.soff + static_cast<int>(TPL * m * row_bytes));
+                    for (int m = 0; m < KM; ++m) {
+                        const bool hi = BPC == 2 && m >= KM / 2;
+                        kd[m] = load(hi ? r.kr2 : r.kr, k_lane_off,
+                                     r.soff + static_cast<int>(TPL * (hi ? m - KM / 2 : m) * row_bytes));
+                    }
                 };
                 auto issue_v = [&](uint4 (&vd)[VL], const Src& r) {
 #pragma unroll
-                    for (int v = 0; v < VL; ++v) vd[v] = load(r.vr, v_lane_off, r.soff + static_cast<int>(RPL * v * row_bytes));
+                    for (int v = 0; v < VL; ++v) {
+                        const bool hi = BPC == 2 && v >= VL / 2;
+                        vd[v] = load(hi ? r.vr2 : r.vr, v_lane_off,
+                                     r.soff + static_cast<int>(RPL * (hi ? v - VL / 2 : v) * row_bytes));
+                    }
                 };
 
                 auto consume = [&](uint4 (&kd)[KM], uint4 (&vd)[VL], int k, int k2, bool live2) {
@@ -927,8 +966,8 @@ void decode_mfma_kernel(const DecodeArgs a) {
                     }
                     const Src nxt = source(k2, live2);
                     issue_k(kd, nxt);
-                    const bool need_mask = !cur.blk_ok || (cb + (kw + k) * cs) == c_rag;
-                    const bool tok_ok = cur.blk_ok && t_lane < cur.rem;
+                    const bool need_mask = !(cur.ok_lo && cur.ok_hi) || (cb + (kw + k) * cs) == c_rag;
+                    const bool tok_ok = (t_lane < BS ? cur.ok_lo : cur.ok_hi) && t_lane < cur.rem;
                     const bool b3 = lp & 2, b2 = lp & 1;
                     float pr[RS];
 #pragma unroll
@@ -1315,10 +1354,10 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeArgs
     }
 }
 
-// Matrix cores take groups of 3 to 8 query heads (block >= 16); the vector
-// kernel takes groups of 1 and 2 and block size 8.
+// Matrix cores take groups of 3 to 8 query heads (blocks of 8 tokens or
+// more); the vector kernel takes groups of 1 and 2.
 template <int BS, int G>
-constexpr bool use_mfma() { return BS >= kChunk && G >= 3 && G <= 8; }
+constexpr bool use_mfma() { return (BS >= kChunk || 2 * BS == kChunk) && G >= 3 && G <= 8; }
 
 template <int D, int BS, int G>
 constexpr auto split_kernel() {

@@ -244,6 +244,41 @@ def test_out_of_range_table_entry_is_skipped_not_read():
         pa.pa_set_validate(prev)
 
 
+@pytest.mark.parametrize("bs", [8, 16])
+def test_out_of_range_entries_inside_a_context_drop_their_tokens(bs):
+    """Bad entries at an even and an odd block index of a long context (at
+    block size 8 the first and the second block of a 16-token chunk): their
+    tokens drop out of the softmax, which the oracle reproduces by leaving the
+    two blocks out of the table (attention over a set of rows does not depend
+    on their order)."""
+    wl = W.shrink(MEDIUM, name=f"medium_bad_bs{bs}", block_size=bs,
+                  num_blocks=1024 * 16 // bs, max_blocks_per_seq=4096 // bs)
+    p = build(wl, plan_fn=medium_plan(wl))
+    run_step(p)
+    s = 5                                           # 3333 tokens
+    L = int(p["plan"].context_lens[s])
+    nblk = -(-L // bs)
+    drop = [40, 101]
+    assert max(drop) < nblk - 1
+    bad = p["tables"].clone()
+    for i in drop:
+        bad[s, i] = -1 if i % 2 else wl.num_blocks + 5
+    for n_split in (0, 300):
+        say(f"decode with out-of-range entries, block size {bs}, {n_split} splits")
+        out = pa.pa_decode(p["q"], p["kc"], p["vc"], bad, p["lens"], wl.scale,
+                           max_context_len=p["max_ctx"], num_splits=n_split)
+        torch.cuda.synchronize()
+        kc, vc = oracle_caches(p)
+        r = p["ref"]
+        tables = r["tables"].copy()
+        keep = [i for i in range(tables.shape[1]) if i not in drop]
+        tables[s] = np.concatenate([tables[s, keep], np.full(len(drop), -1, tables.dtype)])
+        lens = r["lens"].copy()
+        lens[s] = L - len(drop) * bs
+        ref = decode_ref(r["q"], kc.view(np.float16), vc.view(np.float16), tables, lens, wl.scale)
+        check_close(out, ref, f"bad entries bs={bs} N={n_split}")
+
+
 # Full-size workloads in the launch configuration the benchmark times (mha on
 # one workgroup per pair, the others on the library's default split); every
 # sequence is compared except in prefix, where 6 of 64 share one prefix.
