@@ -54,10 +54,9 @@
 //  * Software pipelining: the next chunk's K and V loads are issued before
 //    the current chunk is consumed (two register buffers).  The loads carry
 //    the non-temporal hint: every byte is read once per call.  A pair's
-//    ragged last chunk rides the same pipeline where that costs no registers
-//    (one block per chunk, G <= 4): its block's buffer range ends at the
-//    context's last token, so the rows past it read as zeros and are never
-//    fetched.
+//    ragged last chunk rides the same pipeline where it has one block (blocks
+//    of 16 tokens or more): that block's buffer range ends at the context's
+//    last token, so the rows past it read as zeros and are never fetched.
 //  * Both cache layouts (slot-major [block][token][head][dim] and head-major
 //    [block][head][token][dim]) run the same code: only the stride between a
 //    head's consecutive token rows and the head's offset in a block differ.
@@ -84,12 +83,10 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kChunk = 16;         // tokens per chunk
-// Occupancy (waves per SIMD) the register allocator of the vector kernel may
-// trade down to while keeping two chunks of K and V in registers: 4 waves (128
-// VGPRs) for 1-2 query heads per KV head, 3 (168) for 4, 2 (256) for the other
-// groups (which reach this kernel only with blocks of 8 tokens).
-template <int G>
-constexpr int waves_per_simd() { return G <= 2 ? 4 : (G == 4 ? 3 : 2); }
+// Occupancy (waves per SIMD) of the vector kernel, which serves 1-2 query
+// heads per KV head: 4 waves (128 VGPRs) with two chunks of K and V in
+// registers.
+constexpr int kVectorWavesPerSimd = 4;
 constexpr float kNegBig = -1.0e30f;  // start value of a running max
 // Word 3 of a gfx9-family buffer resource: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -206,8 +203,9 @@ struct Geometry {
 };
 
 template <int D, int BS, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<G>())))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kVectorWavesPerSimd)))
 void decode_split_kernel(const DecodeArgs a) {
+    static_assert(G >= 1 && G <= 2, "3 to 8 query heads per KV head run on decode_mfma_kernel");
     using Geo = Geometry<D>;
     constexpr int LPR = Geo::LPR;
     constexpr int RPL = Geo::RPL;
@@ -216,10 +214,10 @@ void decode_split_kernel(const DecodeArgs a) {
     constexpr int kPerBlock = LPC / BPC;                  // granules of a chunk per block
     static_assert(BS % RPL == 0, "a load must not straddle two blocks");
     // The pair's ragged last chunk goes through the load pipeline (its rows
-    // past the context read as zeros through a shortened buffer range) where
-    // that costs no registers: one block per chunk and G <= 4.  Otherwise it
-    // is loaded after the pipeline and its rows are dropped in registers.
-    constexpr bool kFold = BS >= kChunk && G <= 4;
+    // past the context read as zeros through a shortened buffer range) when
+    // it lies in one block.  Otherwise it is loaded after the pipeline and
+    // its rows are dropped in registers.
+    constexpr bool kFold = BS >= kChunk;
 
     __shared__ float s_acc[kWaves][G][D];
     __shared__ float s_m[kWaves][G];
