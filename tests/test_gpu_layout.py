@@ -73,14 +73,17 @@ def test_head_major_store_matches_oracle():
     assert np.array_equal(host_u16(vc), ref_v)
 
 
-# (seed, block size, KV heads, head dim, group, lengths): block 16 takes the
-# folded ragged path, block 8 and group 8 the separate masked one.
+# (seed, block size, KV heads, head dim, group, lengths): groups of 1 and 2 on
+# the vector kernel (block 8: the ragged chunk on its separate masked path),
+# the others on the matrix-core kernel (block 8: two blocks a chunk).
 DECODE = [
     (1, 16, 4, 128, 4, [1, 17, 200, 777, 1000, 33]),
     (2, 8, 2, 128, 4, [5, 300, 64, 129]),
     (3, 32, 2, 64, 1, [31, 500, 1, 96]),
     (4, 16, 2, 128, 8, [400, 15, 250]),
     (5, 64, 8, 128, 1, [2048, 2048, 1999, 70]),
+    (6, 8, 3, 64, 2, [9, 1000, 255, 8]),
+    (7, 8, 4, 64, 6, [16, 7, 333, 1024]),
 ]
 
 
