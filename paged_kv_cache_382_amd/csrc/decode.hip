@@ -626,13 +626,15 @@ void decode_split_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core variant for 3 to 8 query heads per KV head (block size >= 16).
+// Matrix-core variant for 3 to 8 query heads per KV head (blocks of 8 tokens
+// or more; at block 8 a 16-token chunk takes two table entries).
 //
 // Same partition, workspace and merge as decode_split_kernel, except that on
-// the slot-major layout with a multiple of 4 KV heads a sequence's part of the
-// chunk list may run in the head-group order (groups of 4 heads, chunk-major
-// inside a group, one head per wave; see hg_mode below), whose partial slots
-// are 4 * (split + group) + head in group.  The work on a segment:  The G query rows of a KV head are the rows of
+// the slot-major layout with a multiple of 4 KV heads (blocks of 16 or more) a
+// sequence's part of the chunk list may run in the head-group order (groups of
+// 4 heads, chunk-major inside a group, one head per wave; see hg_mode below),
+// whose partial slots are 4 * (split + group) + head in group.  The work on a
+// segment: the G query rows of a KV head are the rows of
 // v_mfma_f32_4x4x4_16b_f16 tiles (one set of 4 rows for G <= 4, two for
 // G <= 8; rows past G hold zero queries and are never written), so that the
 // products run on the matrix cores and the vector ALUs only keep the
