@@ -652,13 +652,10 @@ def run_decode(wl, dev, layout="slot", splits_arg=0, steps=20, warmup=3, layers=
     cows = torch.tensor([list(c) for c in plan.cow_pairs], dtype=torch.int32,
                         device=dev).reshape(-1, 2)
     desc = pa.cache_desc(caches[0][0], layout)
-    splits = splits_arg                 # 0: the library's choice for this batch
-    if (splits == 0 and B <= 64 and min(lens) == max(lens)
-            and B * hkv >= pa.pa_decode_num_splits(desc, hq, 0)):
-        # The host knows the lengths: all equal, and the pairs alone fill the
-        # device, so the balanced split is one workgroup per (sequence, KV head)
-        # pair and the merge would find nothing; ask for that partition.
-        splits = -1
+    # 0: the library's own partition for this batch.  No hint is passed for
+    # equal lengths: one workgroup per pair (-1) measured slower on mha than
+    # the default of two workgroups a compute unit, each taking two whole pairs.
+    splits = splits_arg
     ws = pa.decode_workspace(desc, B, hq, splits, dev)
 
     def step(events=None):
@@ -741,7 +738,7 @@ def run_decode(wl, dev, layout="slot", splits_arg=0, steps=20, warmup=3, layers=
             "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
             "context_min": min(lens), "context_max": max_ctx, "context_sum": sum(lens),
             "layers": layers,
-            "num_splits": {0: "auto", -1: "whole pairs (equal contexts)"}.get(splits, splits),
+            "num_splits": {0: "auto", -1: "whole pairs"}.get(splits, splits),
             "pool_blocks": wl.num_blocks,
             "cache_layout": LAYOUT_NAMES[layout],
             "parallelism": "single GPU",
@@ -835,6 +832,8 @@ def main():
                     help="skip the streaming-read probe on layer 0's caches")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="prefill: skip timing the matrix-core probe")
+    ap.add_argument("--no-whole-pair", dest="with_whole_pair", action="store_false",
+                    help="with mha at the default partition, skip timing one workgroup per pair beside it")
     ap.add_argument("--no-mix", dest="with_mix", action="store_false",
                     help="with the default mha workload, skip the second measured configuration "
                          "(mixed context lengths, reported under 'mix')")
@@ -874,11 +873,11 @@ def main():
     result, st = run_decode(wl, dev, args.layout, args.splits, args.steps, args.warmup, layers,
                             args.graph, not args.no_read_ceiling,
                             0.0 if args.no_cpu_baseline else args.cpu_budget)
-    if wl.name == "mha" and st["splits"] == -1 and args.splits == 0:
-        # The headline asks for one workgroup per pair (all contexts equal);
-        # report the library's own choice for the same batch beside it.
-        result["library_default_partition"] = time_decode_only(
-            wl, st, args.layout, 0, max(args.steps // 2, 5), args.warmup)
+    if wl.name == "mha" and args.splits == 0 and args.with_whole_pair:
+        # The headline runs the library's own partition; beside it, the same
+        # batch with one workgroup per pair (-1, which equal contexts allow).
+        result["whole_pair_partition"] = time_decode_only(
+            wl, st, args.layout, -1, max(args.steps // 2, 5), args.warmup)
     if wl.name == "mha" and args.with_mix:
         # The second configuration the target names: mixed context lengths.
         del st

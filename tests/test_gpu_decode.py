@@ -279,14 +279,14 @@ def test_out_of_range_entries_inside_a_context_drop_their_tokens(bs):
         check_close(out, ref, f"bad entries bs={bs} N={n_split}")
 
 
-# Full-size workloads in the launch configuration the benchmark times (mha on
-# one workgroup per pair, the others on the library's default split); every
-# sequence is compared except in prefix, where 6 of 64 share one prefix.
-FULL = [("mha", None, -1), ("mix", None, 0), ("prefix", [0, 15, 31, 47, 62, 63], 0),
+# Full-size workloads in the launch configuration the benchmark times (the
+# library's default partition), and mha also on one workgroup per pair (-1);
+# every sequence is compared except in prefix, where 6 of 64 share one prefix.
+FULL = [("mha", None, 0), ("mha", None, -1), ("mix", None, 0), ("prefix", [0, 15, 31, 47, 62, 63], 0),
         ("long_bs16", None, 0), ("long_bs8", None, 0), ("long_bs64", None, 0)]
 
 
-@pytest.mark.parametrize("name,seqs,n_split", FULL, ids=[f[0] for f in FULL])
+@pytest.mark.parametrize("name,seqs,n_split", FULL, ids=[f"{f[0]}_N{f[2]}" for f in FULL])
 def test_decode_full_size(name, seqs, n_split):
     wl = W.ALL.get(name) or W.long_workload(int(name.split("bs")[1]))
     p = build(wl, fill="random")
